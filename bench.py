@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Throughput of the head-scale KV-pruning hot path on one MI355X.
+
+A step is one generation pass of the whole hot path over one batch: for every
+scale t = 0..K-1 and every layer, block-causal attention over the kept cache
+segments plus the current scale (hk_attend), and after every scale but the
+last, one compaction of all layers' kept segments into the ragged cache
+(hk_append_scale).  Inputs are synthetic and already resident in HBM when the
+timed region starts.
+
+Default workload: one Infinity-2B-shaped layer at full cache (16 heads,
+head_dim 128, batch 1, 13 scales with sides 1..64, 10,521 tokens), bf16.
+``value`` is attention TFLOP/s over the whole pass (algorithmic flops
+4*d*n_q*n_k summed over all attention launches, divided by the pass time).
+
+Also reported: the attention kernel's roofline (MFMA bf16), compaction GB/s,
+the 32-layer batch-8 10%-budget workload's scales/s per image, and the fp64
+CPU oracle timed on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("attend TFLOP/s + % bf16 MFMA peak; compact GB/s; scales/sec per image at 10% budget")
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+ATTEND_SOURCES = ["kv_cache_compression_attend_amd/csrc/attend_bf16.hip",
+                  "kv_cache_compression_attend_amd/csrc/device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_bf16_infinity2b_layer_traffic.json")
+
+
+def attend_sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pruned", action="store_true",
+                    help="skip the 32-layer 10%%-budget scales/s measurement")
+    ap.add_argument("--pruned-steps", type=int, default=5)
+    ap.add_argument("--cpu-heads", type=int, default=4,
+                    help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
+    return ap.parse_args()
+
+
+def pass_flops(wl, keep, lenb_fn):
+    """Algorithmic attention flops of each (layer, step) launch: sum over (b, h)
+    of 4 * d * n_t * (cached keys + n_t)."""
+    out = {}
+    for l in range(wl.layers):
+        for t in range(wl.n_scales):
+            n = wl.scale_tokens[t]
+            keys = lenb_fn(t)[l] + n          # [H]
+            out[(l, t)] = 4.0 * wl.head_dim * n * float(keys.sum()) * wl.batch
+    return out
+
+
+def compact_bytes(wl, keep, t, layers):
+    """Algorithmic bytes of one compaction launch: read + write of every kept segment."""
+    kept = int(keep[layers, :, t].sum()) if t <= wl.n_scales - 2 else 0
+    elem = 2 if wl.dtype == "bf16" else 4
+    return 2.0 * 2.0 * kept * wl.batch * wl.scale_tokens[t] * wl.head_dim * elem
+
+
+def lenb_table(keep, tokens):
+    import numpy as np
+    L, H, K = keep.shape
+
+    def f(t):
+        out = np.zeros((L, H), dtype=np.int64)
+        for s in range(min(t, K - 1)):
+            out += keep[:, :, s].astype(np.int64) * tokens[s]
+        return out
+    return f
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kv_cache_compression_attend_amd as hk
+    import workloads
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------- main workload: one full-cache Infinity-2B-shaped layer ----------------
+    wl = workloads.get("c1")
+    table = workloads.dirichlet_scas(wl)
+    keep, _, _ = hk.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
+    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
+                     torch.bfloat16)
+    K, L = wl.n_scales, wl.layers
+    qs, kall, vall, outs = [], [], [], []
+    for t in range(K):
+        ins = [workloads.step_inputs(wl, l, t) for l in range(L)]
+        to = lambda a: torch.from_numpy(np.stack(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa
+        qs.append(to([x.q for x in ins]))
+        kall.append(to([x.k for x in ins]))
+        vall.append(to([x.v for x in ins]))
+        outs.append(torch.empty_like(qs[-1][0]))
+    flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
+    total_flops = sum(flops.values())
+
+    def one_pass(rec=None):
+        ctx.reset()
+        for t in range(K):
+            for l in range(L):
+                if rec is not None:
+                    rec[("a", l, t)][0].record(stream)
+                ctx.attend(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                           stream=stream)
+                if rec is not None:
+                    rec[("a", l, t)][1].record(stream)
+            if t < K - 1:
+                if rec is not None:
+                    rec[("c", t)][0].record(stream)
+                if L == 1:
+                    ctx.append_scale(0, 1, t, kall[t][0], vall[t][0], stream=stream)
+                else:
+                    ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+                if rec is not None:
+                    rec[("c", t)][1].record(stream)
+
+    for _ in range(args.warmup):
+        one_pass()
+    torch.cuda.synchronize()
+
+    # timed passes (whole-pass clock), then the same number of passes with per-launch events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        one_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_pass = t0.elapsed_time(t1) / args.steps
+
+    recs = []
+    for _ in range(args.steps):
+        rec = {}
+        for t in range(K):
+            for l in range(L):
+                rec[("a", l, t)] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            if t < K - 1:
+                rec[("c", t)] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        one_pass(rec)
+        recs.append(rec)
+    torch.cuda.synchronize()
+    attend_ms = {key: np.mean([r[key][0].elapsed_time(r[key][1]) for r in recs])
+                 for key in recs[0] if key[0] == "a"}
+    compact_ms = {key: np.mean([r[key][0].elapsed_time(r[key][1]) for r in recs])
+                  for key in recs[0] if key[0] == "c"}
+    attend_total_ms = sum(attend_ms.values())
+    attend_tflops = total_flops / (attend_total_ms * 1e-3) / 1e12
+    n_launch = len(attend_ms)
+    per_step = {t: round(flops[(0, t)] / (attend_ms[("a", 0, t)] * 1e-3) / 1e12, 1) for t in range(K)}
+    cbytes = {t: compact_bytes(wl, keep, t, slice(0, L)) for t in range(K - 1)}
+    compact_gbps = sum(cbytes.values()) / (sum(compact_ms.values()) * 1e-3) / 1e9
+    c_big = max(cbytes, key=lambda t: cbytes[t])
+    compact_big_gbps = cbytes[c_big] / (compact_ms[("c", c_big)] * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_sha256") == attend_sources_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    value = total_flops / (ms_pass * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_pass, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) draws rounded to bf16; no model weights)",
+        "config": {"workload": "infinity2b-layer-full-b1: 1 layer x 16 heads x head_dim 128, "
+                               "batch 1, 13 scales (sides 1..64, 10,521 tokens), 100% budget; "
+                               "13 attention launches + 12 compactions per step",
+                   "global_batch": wl.batch, "seq_len": wl.total_tokens,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "attend_bf16_d128_kernel<false>",
+                     "achieved": round(attend_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attend_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "avg_launch_us": round(attend_total_ms / n_launch * 1e3, 2),
+                     "flops_per_launch": total_flops / n_launch},
+        "attend_tflops_per_step": per_step,
+        "compact": {"GBps": round(compact_gbps, 1), "frac_hbm": round(compact_gbps / PEAK_HBM_GBPS, 4),
+                    "largest_step": c_big, "largest_step_GBps": round(compact_big_gbps, 1)},
+    }
+    ctx.close()
+    del qs, kall, vall, outs
+    torch.cuda.empty_cache()
+
+    # ---------------- 32 layers, batch 8, 10% budget: scales/s per image ----------------
+    if not args.no_pruned:
+        result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
+
+    # ---------------- fp64 CPU oracle on a bounded sample ----------------
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args, wl, keep)
+    print(json.dumps(result), flush=True)
+
+
+def pruned_rate(args, hk, workloads, torch, np, dev, stream):
+    """Whole-pass rate of the 32-layer, batch-8, 10%-budget workload."""
+    wl = workloads.get("c2")
+    keep, ret, n_pruned = hk.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens,
+                                            wl.budget, wl.n_sink)
+    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
+                     torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    K, L = wl.n_scales, wl.layers
+    qs, kall, vall, outs = [], [], [], []
+    for t in range(K):
+        shape = (L, wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim)
+        qs.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        kall.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        vall.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        outs.append(torch.empty(shape[1:], dtype=torch.bfloat16, device=dev))
+    flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
+
+    def one_pass():
+        ctx.reset()
+        for t in range(K):
+            for l in range(L):
+                ctx.attend(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                           stream=stream)
+            if t < K - 1:
+                ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.pruned_steps):
+        one_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.pruned_steps
+    ctx.close()
+    return {"workload": "infinity2b-l32-b8-budget10: 32 layers x 16 heads x d128, batch 8, "
+                        f"10% budget ({n_pruned} of 512 heads pruned per prunable scale)",
+            "ms_per_pass": round(ms, 3),
+            "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
+            "image_scales_per_sec": round(K * wl.batch / (ms * 1e-3), 1),
+            "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+            "passes": args.pruned_steps,
+            "inputs": "torch.randn on the GPU (seeded), same distribution as the parity inputs"}
+
+
+def cpu_baseline(args, wl, keep):
+    """The fp64 oracle, as it stands, on every scale of the first few heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads
+    from oracle import attention as oatt
+    from oracle.numerics import to_f64
+
+    heads = list(range(min(args.cpu_heads, wl.heads)))
+    steps = [workloads.step_inputs(wl, 0, t) for t in range(wl.n_scales)]
+    flops = 0.0
+    start = time.perf_counter()
+    for t in range(wl.n_scales):
+        for h in heads:
+            kj, vj, src, lens = oatt.gather_keys([s.k for s in steps[: t + 1]],
+                                                 [s.v for s in steps[: t + 1]], keep[0, h], t, 0, h)
+            q = to_f64(steps[t].q[0, :, h, :], "bf16")
+            oatt.softmax_attention(q, to_f64(kj, "bf16"), to_f64(vj, "bf16"), wl.softmax_scale)
+            flops += 4.0 * wl.head_dim * q.shape[0] * kj.shape[0]
+    secs = time.perf_counter() - start
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(secs, 2),
+            "sample": f"full-cache layer, batch 1, all 13 scales of heads {heads[0]}..{heads[-1]} "
+                      f"({len(heads)} of {wl.heads}), fp64 NumPy"}
+
+
+if __name__ == "__main__":
+    main()

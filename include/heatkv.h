@@ -1,0 +1,185 @@
+/*
+ * heatkv.h - C ABI of the MI355X (gfx950) head-scale KV-pruning hot path.
+ *
+ * What the library computes (sources are the pages the method is described on):
+ *   - Next-scale generation: a visual autoregressive model emits token maps of
+ *     growing size, one scale at a time, every token of a scale conditioned on
+ *     all earlier scales; the KV cache grows with every scale (HeatKV project
+ *     page, Abstract; Pith page of arXiv 2605.14877, Figure 2 caption).  Tokens
+ *     inside a scale are in raster order (same page, Figure 3 caption).
+ *   - Head-scale pruning: whole (layer, head, source-scale) segments are
+ *     removed from the cache by a static schedule built offline from S-CAS,
+ *     the attention mass each head puts on each earlier scale; early sink
+ *     scales are always kept (HeatKV project page, Method steps 2-5; Pith
+ *     page, Figure 4 caption).
+ *
+ * Vocabulary and shapes used below:
+ *   L layers, H heads, D head_dim, B batch, K scales with n_s tokens each.
+ *   keep[l][h][s] (uint8) = 1 when segment s of head (l, h) is cached once
+ *   scale s completes.  The final scale K-1 is never cached; keep[.][.][K-1]
+ *   is ignored.
+ *   Per-scale tensors q, k_cur, v_cur, out are [B][n_t][H][D], contiguous,
+ *   row-major, of the context's dtype.
+ *
+ * Cache layout (the caller allocates two buffers, one for K and one for V,
+ * of hk_layout()'s size; the library only writes and reads them):
+ *   cap[l][h]  = sum of n_s over s <= K-2 with keep[l][h][s] = 1;
+ *   heads are laid out one after another in row-major (l, h) order and head
+ *   (l, h) owns B * cap[l][h] * D elements, as [B][cap[l][h]][D];
+ *   after scale k has been appended, rows [0, len_before(l,h,k+1)) of (l,h,b)
+ *   hold the kept segments s <= k in scale order, where
+ *   len_before(l,h,t) = sum of n_s over kept s < t.
+ *
+ * Conventions:
+ *   - Every function returns HK_OK (0) or a negative HK_E* status and never
+ *     aborts; hk_last_error() returns this thread's text of the last failure.
+ *   - Device pointers are HIP device memory on the context's device, 16-byte
+ *     aligned.  hip_stream is a hipStream_t (NULL = the null stream).  Device
+ *     work is enqueued asynchronously on that stream; faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - The library allocates device memory only in hk_create (small tables and
+ *     S-CAS partial sums) and frees it in hk_destroy; nothing allocates on the
+ *     per-scale calls.
+ *   - A context is not thread-safe: calls on one context must be serialised
+ *     by the caller.
+ */
+#ifndef HEATKV_H
+#define HEATKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define HK_OK 0
+#define HK_EINVAL (-1)        /* bad argument: shape, range, null, alignment */
+#define HK_EBUDGET (-2)       /* budget below the cost of the sink scales */
+#define HK_EORDER (-3)        /* per-layer scale order violated */
+#define HK_EHIP (-4)          /* HIP runtime or launch error */
+#define HK_EUNSUPPORTED (-5)  /* dtype / head_dim combination not compiled */
+
+/* element types */
+#define HK_DTYPE_F32 0
+#define HK_DTYPE_BF16 1
+
+/* compile-time limits */
+#define HK_MAX_SCALES 16
+
+typedef struct hk_ctx hk_ctx; /* opaque; owned by the library */
+
+/* Text of this thread's last non-OK return ("" if none). Owned by the library,
+ * valid until the next call on this thread. */
+const char* hk_last_error(void);
+
+/* Build the static keep-mask from an S-CAS table and a memory budget.
+ *
+ * Follows the HeatKV project page, Method steps 3-5 (rank head-scale pairs by
+ * their contribution to future predictions; remove low-ranked pairs to meet
+ * the budget; keep the early sink scales; one static, prompt-independent
+ * schedule) and the Figure 4 caption of the Pith page of arXiv 2605.14877
+ * (per-source-scale orderings O_i of the heads from least to most dependent,
+ * pruning set = union of a prefix of each O_i).  Readings taken:
+ *   importance(l,h,s) = sum over t = s+1..K-1 of scas[l][h][t][s], summed in
+ *     double in ascending t;
+ *   prunable scales are n_sink..K-2, each with ordering O_s of the flat head
+ *     index f = l*H+h ascending by (importance, f);
+ *   F = L*H*sum_{s<=K-2} n_s, budget = floor(budget_frac * F) token slots;
+ *   heads kept per prunable scale = min(L*H, floor((budget - sink cost) /
+ *     sum of n_s over prunable s)); N = L*H - that; the first N heads of each
+ *     O_s are dropped (greedy early pruning with one prefix length).
+ *
+ *   scale_tokens  host int32 [K], n_s >= 1
+ *   scas          host float [L][H][K][K], row t over sources s <= t
+ *   budget_frac   in (0, 1]
+ *   n_sink        in [0, K-1]
+ *   keep_out      host uint8 [L][H][K] (written; keep_out[.][.][K-1] = 0)
+ *   retained_out  host int64 [K] or NULL: token slots per sequence held after
+ *                 each scale k (sum over kept s <= min(k, K-2) of n_s)
+ *   n_pruned_out  host int32 or NULL: N
+ * Errors: HK_EINVAL (bad sizes, ranges, NULL), HK_EBUDGET (budget below the
+ * sink cost).  K <= HK_MAX_SCALES is not required here. */
+int hk_build_schedule(int L, int H, int K, const int32_t* scale_tokens, const float* scas,
+                      double budget_frac, int n_sink, uint8_t* keep_out,
+                      int64_t* retained_out, int32_t* n_pruned_out);
+
+/* Size of one cache buffer (K or V; both have the same size) for a keep-mask,
+ * in elements, and optionally the per-head capacities and element offsets of
+ * the layout described at the top of this file.
+ *   cache_elems_out  host int64 (required)
+ *   cap_out          host int64 [L][H] or NULL
+ *   base_out         host int64 [L][H] or NULL
+ * Errors: HK_EINVAL. */
+int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* keep,
+              int B, int D, int64_t* cache_elems_out, int64_t* cap_out, int64_t* base_out);
+
+/* Create a context on the current HIP device.  Copies scale_tokens and keep,
+ * and uploads the small per-head tables.  k_cache / v_cache are caller-owned
+ * device buffers of hk_layout() elements each; they must outlive the context.
+ * Supported: dtype HK_DTYPE_BF16 with D = 128 (matrix-core path), and
+ * HK_DTYPE_F32 with D in {16, 32, 64, 128}; K <= HK_MAX_SCALES.
+ * Errors: HK_EINVAL, HK_EUNSUPPORTED, HK_EHIP (allocation or copy failed). */
+int hk_create(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
+              const uint8_t* keep, int dtype, void* k_cache, void* v_cache);
+
+/* Free the context's device tables (synchronises the device first). NULL is OK. */
+int hk_destroy(hk_ctx* ctx);
+
+/* Start a new generation: every layer's cache is considered empty again. */
+int hk_reset(hk_ctx* ctx);
+
+/* Block-causal attention of scale `step` in `layer`.
+ *
+ * For every (b, h) and query i of scale step:
+ *   out[b][i][h][:] = softmax_j(softmax_scale * q[b][i][h][:] . key_j) value_j
+ * over the keys j of the kept segments s < step of head (layer, h), read from
+ * the cache in scale order, followed by the n_step keys of k_cur[b][:][h][:]
+ * (the scale being generated).  Scores and the softmax are fp32; with bf16
+ * the products run on the matrix cores, probabilities are rounded to bf16 for
+ * the value product, and out is rounded to bf16 (nearest even).
+ * Order: requires that hk_append_scale has covered (layer, step-1) since the
+ * last hk_reset (not needed for step 0).
+ * Errors: HK_EINVAL, HK_EORDER, HK_EHIP. */
+int hk_attend(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,
+              const void* v_cur, void* out, float softmax_scale, void* hip_stream);
+
+/* hk_attend, plus this step's S-CAS row (HeatKV project page, Abstract and
+ * Method step 2: attention probabilities aggregated per layer, head, source
+ * scale and future scale).  Reading taken: for each query of scale step, the
+ * probability mass on the keys of source s, averaged over the n_step queries
+ * and then over the batch:
+ *   scas_table[layer][h][step][s], s = 0..step, overwritten for every h;
+ * dropped sources get exactly 0; entries s > step are not written.
+ *   scas_table  device float [L][H][K][K]
+ * The cross-workgroup sum runs in a fixed order (deterministic).
+ * Errors: as hk_attend. */
+int hk_attend_with_scas(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,
+                        const void* v_cur, void* out, float softmax_scale,
+                        float* scas_table, void* hip_stream);
+
+/* Compact scale `step` into the cache for layers [layer_begin, layer_end):
+ * for every kept (l, h) (keep[l][h][step] = 1) and every b, copies the rows
+ * k_cur_l[b][:][h][:] (and likewise V) to rows
+ * [len_before(l,h,step), +n_step) of (l, h, b), bit for bit (HeatKV project
+ * page, Method step 5: pruning during inference as scales are generated; a
+ * dropped segment is simply never written).
+ *   k_cur, v_cur        device, layer l's tensor at k_cur + (l - layer_begin)
+ *                       * layer_stride_elems, each [B][n_step][H][D]
+ *   layer_stride_elems  element stride between consecutive layers' tensors
+ *                       (ignored when one layer is given)
+ * Order: each layer's scales must be appended in order 0, 1, ..., K-2 since
+ * the last hk_reset; step = K-1 is rejected (the final scale is never cached).
+ * Errors: HK_EINVAL, HK_EORDER, HK_EHIP. */
+int hk_append_scale(hk_ctx* ctx, int layer_begin, int layer_end, int step, const void* k_cur,
+                    const void* v_cur, int64_t layer_stride_elems, void* hip_stream);
+
+/* Token slots per sequence held by the whole cache (all layers and heads)
+ * once scale `step` has been appended: sum over kept s <= min(step, K-2). */
+int hk_retained_tokens(const hk_ctx* ctx, int step, int64_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEATKV_H */

@@ -1,0 +1,256 @@
+"""MI355X (gfx950) hot path of head-scale KV-cache pruning for next-scale
+visual autoregressive transformers: Python binding of ``libheatkv.so``.
+
+The binding only marshals arguments: every step of the path (schedule,
+attention, S-CAS, compaction) runs in the C/HIP library declared in
+``include/heatkv.h``.  PyTorch provides device memory and streams.  There is
+no CPU fallback: importing this package fails if the library is not built.
+
+Typical use for one generation (all layers, all scales)::
+
+    keep, retained, n_pruned = build_schedule(scas_table, tokens, 0.10, n_sink=2)
+    ctx = Context(L, H, D, B, tokens, keep, torch.bfloat16)   # allocates the caches
+    for t in range(K):
+        for l in range(L):
+            ctx.attend(l, t, q, k, v, out, softmax_scale)
+        if t < K - 1:
+            ctx.append_scale(0, L, t, k_all_layers, v_all_layers, layer_stride)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch  # first: the library binds to the HIP runtime torch has loaded
+
+__all__ = ["HeatKVError", "build_schedule", "layout", "Context", "library_path", "DTYPES"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libheatkv.so")
+
+HK_OK, HK_EINVAL, HK_EBUDGET, HK_EORDER, HK_EHIP, HK_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+STATUS_NAMES = {HK_EINVAL: "EINVAL", HK_EBUDGET: "EBUDGET", HK_EORDER: "EORDER",
+                HK_EHIP: "EHIP", HK_EUNSUPPORTED: "EUNSUPPORTED"}
+HK_DTYPE_F32, HK_DTYPE_BF16 = 0, 1
+DTYPES = {torch.float32: HK_DTYPE_F32, torch.bfloat16: HK_DTYPE_BF16}
+
+
+class HeatKVError(RuntimeError):
+    """A non-OK status from the library; ``status`` is the HK_E* code."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m kv_cache_compression_attend_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, I64, D, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
+    sig = {
+        "hk_last_error": ([], ctypes.c_char_p),
+        "hk_build_schedule": ([I, I, I, P, P, D, I, P, P, P], I),
+        "hk_layout": ([I, I, I, P, P, I, I, P, P, P], I),
+        "hk_create": ([P, I, I, I, I, I, P, P, I, P, P], I),
+        "hk_destroy": ([P], I),
+        "hk_reset": ([P], I),
+        "hk_attend": ([P, I, I, P, P, P, P, F, P], I),
+        "hk_attend_with_scas": ([P, I, I, P, P, P, P, F, P, P], I),
+        "hk_append_scale": ([P, I, I, I, P, P, I64, P], I),
+        "hk_retained_tokens": ([P, I, P], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != HK_OK:
+        raise HeatKVError(rc, _lib.hk_last_error().decode(errors="replace"))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def build_schedule(scas: np.ndarray, scale_tokens: Sequence[int], budget_frac: float,
+                   n_sink: int) -> Tuple[np.ndarray, np.ndarray, int]:
+    """S-CAS table [L][H][K][K] (float32) + budget -> (keep u8 [L][H][K], retained int64 [K], N)."""
+    scas = np.ascontiguousarray(scas, dtype=np.float32)
+    if scas.ndim != 4 or scas.shape[2] != scas.shape[3]:
+        raise HeatKVError(HK_EINVAL, "scas must be [L][H][K][K]")
+    L, H, K, _ = scas.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    keep = np.zeros((L, H, K), dtype=np.uint8)
+    ret = np.zeros(K, dtype=np.int64)
+    npr = np.zeros(1, dtype=np.int32)
+    _check(_lib.hk_build_schedule(L, H, K, _ptr(tok), _ptr(scas), float(budget_frac), int(n_sink),
+                                  _ptr(keep), _ptr(ret), _ptr(npr)))
+    return keep, ret, int(npr[0])
+
+
+def layout(scale_tokens: Sequence[int], keep: np.ndarray, batch: int,
+           head_dim: int) -> Tuple[int, np.ndarray, np.ndarray]:
+    """(elements per cache buffer, cap [L][H], element offset [L][H])."""
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    L, H, K = keep.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    elems = np.zeros(1, dtype=np.int64)
+    cap = np.zeros((L, H), dtype=np.int64)
+    base = np.zeros((L, H), dtype=np.int64)
+    _check(_lib.hk_layout(L, H, K, _ptr(tok), _ptr(keep), int(batch), int(head_dim), _ptr(elems),
+                          _ptr(cap), _ptr(base)))
+    return int(elems[0]), cap, base
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Context:
+    """A library context for one model (L layers x H heads) and one batch shape.
+
+    Allocates the two ragged caches (K and V) with PyTorch on the current
+    device unless ``k_cache``/``v_cache`` are given, and keeps them alive for
+    the context's lifetime.
+    """
+
+    def __init__(self, layers: int, heads: int, head_dim: int, batch: int,
+                 scale_tokens: Sequence[int], keep: np.ndarray, dtype: torch.dtype,
+                 k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
+                 device=None):
+        if dtype not in DTYPES:
+            raise HeatKVError(HK_EUNSUPPORTED, f"dtype {dtype} not supported")
+        self.L, self.H, self.D, self.B = int(layers), int(heads), int(head_dim), int(batch)
+        self.tokens = tuple(int(x) for x in scale_tokens)
+        self.K = len(self.tokens)
+        self.dtype = dtype
+        self.keep = np.ascontiguousarray(keep, dtype=np.uint8)
+        if self.keep.shape != (self.L, self.H, self.K):
+            raise HeatKVError(HK_EINVAL, "keep must be [L][H][K]")
+        self.cache_elems, self.cap, self.base = layout(self.tokens, self.keep, self.B, self.D)
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        n_alloc = max(self.cache_elems, 1)
+        if k_cache is None:
+            k_cache = torch.empty(n_alloc, dtype=dtype, device=dev)
+        if v_cache is None:
+            v_cache = torch.empty(n_alloc, dtype=dtype, device=dev)
+        for c in (k_cache, v_cache):
+            if c.dtype != dtype or not c.is_cuda or not c.is_contiguous() or c.numel() < self.cache_elems:
+                raise HeatKVError(HK_EINVAL, "cache buffers must be contiguous device tensors "
+                                             "of the context dtype with hk_layout() elements")
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.device = k_cache.device
+        tok = np.ascontiguousarray(self.tokens, dtype=np.int32)
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(_lib.hk_create(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
+                                  _ptr(tok), _ptr(self.keep), DTYPES[dtype],
+                                  ctypes.c_void_p(k_cache.data_ptr()),
+                                  ctypes.c_void_p(v_cache.data_ptr())))
+        self._h = handle
+
+    # -- argument checks (shapes the kernels and their grids assume) -------------------
+    def _step_tensor(self, x: torch.Tensor, step: int, name: str) -> ctypes.c_void_p:
+        want = (self.B, self.tokens[step], self.H, self.D)
+        if not isinstance(x, torch.Tensor) or tuple(x.shape) != want:
+            raise HeatKVError(HK_EINVAL, f"{name} must have shape {want}")
+        if x.dtype != self.dtype or x.device != self.device or not x.is_contiguous():
+            raise HeatKVError(HK_EINVAL, f"{name} must be a contiguous {self.dtype} tensor on {self.device}")
+        return ctypes.c_void_p(x.data_ptr())
+
+    def _handle(self):
+        if self._h is None:
+            raise HeatKVError(HK_EINVAL, "context is closed")
+        return self._h
+
+    # -- entry points -------------------------------------------------------------------
+    def reset(self) -> None:
+        _check(_lib.hk_reset(self._handle()))
+
+    def attend(self, layer: int, step: int, q, k, v, out, softmax_scale: float,
+               stream=None) -> None:
+        if not (0 <= step < self.K):
+            raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+        args = [self._step_tensor(t, step, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+        _check(_lib.hk_attend(self._handle(), int(layer), int(step), *args, float(softmax_scale),
+                              _stream(stream)))
+
+    def attend_with_scas(self, layer: int, step: int, q, k, v, out, softmax_scale: float,
+                         scas_table: torch.Tensor, stream=None) -> None:
+        if not (0 <= step < self.K):
+            raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+        args = [self._step_tensor(t, step, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+        want = (self.L, self.H, self.K, self.K)
+        if (tuple(scas_table.shape) != want or scas_table.dtype != torch.float32
+                or scas_table.device != self.device or not scas_table.is_contiguous()):
+            raise HeatKVError(HK_EINVAL, f"scas_table must be a contiguous float32 {want} device tensor")
+        _check(_lib.hk_attend_with_scas(self._handle(), int(layer), int(step), *args,
+                                        float(softmax_scale), ctypes.c_void_p(scas_table.data_ptr()),
+                                        _stream(stream)))
+
+    def append_scale(self, layer_begin: int, layer_end: int, step: int, k, v,
+                     stream=None) -> None:
+        """Compact scale ``step`` of layers [layer_begin, layer_end).
+
+        With one layer, k and v are [B][n][H][D]; with several, they are
+        [layers][B][n][H][D] (one contiguous tensor per layer range).
+        """
+        nl = int(layer_end) - int(layer_begin)
+        if not (0 <= step < self.K):
+            raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+        per = (self.B, self.tokens[step], self.H, self.D)
+        stride = 0
+        ptrs = []
+        for t, nm in ((k, "k"), (v, "v")):
+            shape = per if nl == 1 and t.dim() == 4 else (nl,) + per
+            if tuple(t.shape) != shape or t.dtype != self.dtype or t.device != self.device \
+                    or not t.is_contiguous():
+                raise HeatKVError(HK_EINVAL, f"{nm} must be a contiguous {self.dtype} tensor of shape {shape}")
+            ptrs.append(ctypes.c_void_p(t.data_ptr()))
+            stride = int(np.prod(per))
+        _check(_lib.hk_append_scale(self._handle(), int(layer_begin), int(layer_end), int(step),
+                                    ptrs[0], ptrs[1], stride if nl > 1 else 0, _stream(stream)))
+
+    def retained_tokens(self, step: int) -> int:
+        out = ctypes.c_int64()
+        _check(_lib.hk_retained_tokens(self._handle(), int(step), ctypes.byref(out)))
+        return int(out.value)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            h, self._h = self._h, None
+            _check(_lib.hk_destroy(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

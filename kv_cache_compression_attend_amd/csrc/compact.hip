@@ -1,0 +1,65 @@
+// Compaction: copy the kept (layer, head) segments of a completed scale into
+// the ragged per-head cache (HeatKV project page, Method step 5: pruning
+// during inference as new scales are generated; a pruned segment is simply
+// never written).
+//
+// A pure copy, bound by HBM bandwidth.  Each workgroup moves one block of
+// rows of one (segment, batch entry) for both K and V; every lane moves
+// 16-byte vectors, 16 lanes cover one 256-byte row, and each lane keeps
+// several loads in flight before storing.
+#include "device.h"
+
+namespace hk {
+
+constexpr int kCopyThreads = 256;
+constexpr int kCopyItems = 4;   // 16-byte vectors per lane per tensor
+
+__global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
+  const int chunk = blockIdx.x % a.chunks;
+  const int rest = blockIdx.x / a.chunks;
+  const int b = rest % a.B;
+  const int di = rest / a.B;
+  const CopyDesc d = a.desc[di];
+
+  const int cpr = a.row_bytes >> 4;                 // vectors per row
+  const int row0 = chunk * a.rows_per_block;
+  const int rows = min(a.rows_per_block, a.n - row0);
+  const int items = rows * cpr;
+
+  const int64_t tok_stride = int64_t(a.H) * a.row_bytes;
+  const int64_t src0 = int64_t(d.layer - a.layer_begin) * a.layer_stride_bytes +
+                       (int64_t(b) * a.n + row0) * tok_stride + int64_t(d.head) * a.row_bytes;
+  const int64_t dst_row0 = d.dst + (int64_t(b) * d.cap + row0) * a.row_bytes;
+
+  for (int base = threadIdx.x; base < items; base += kCopyThreads * kCopyItems) {
+    uint4 kv[kCopyItems], vv[kCopyItems];
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      const int it = base + u * kCopyThreads;
+      if (it < items) {
+        const int r = it / cpr, c = it % cpr;
+        const int64_t off = src0 + r * tok_stride + c * 16;
+        kv[u] = *reinterpret_cast<const uint4*>(a.kcur + off);
+        vv[u] = *reinterpret_cast<const uint4*>(a.vcur + off);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      const int it = base + u * kCopyThreads;
+      if (it < items) {
+        const int64_t off = dst_row0 + int64_t(it) * 16;
+        *reinterpret_cast<uint4*>(a.kcache + off) = kv[u];
+        *reinterpret_cast<uint4*>(a.vcache + off) = vv[u];
+      }
+    }
+  }
+}
+
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
+  const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hk

@@ -1,0 +1,337 @@
+// Context and per-scale entry points of the C ABI: argument checks, the
+// per-layer scale-order state, the small device tables and the kernel
+// launches.  Every entry point returns a status code and records text for
+// hk_last_error(); nothing here aborts.
+#include <math.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/heatkv.h"
+#include "device.h"
+#include "status.h"
+
+struct hk_ctx {
+  int L, H, D, B, K, dtype, device;
+  int elem_bytes;
+  std::vector<int32_t> tokens;
+  std::vector<uint8_t> keep;      // [L][H][K]
+  std::vector<int64_t> cap;       // [L][H]
+  std::vector<int64_t> base;      // [L][H] element offsets
+  std::vector<int32_t> lenb;      // [L][H][K] rows cached before scale t
+  std::vector<int64_t> retained;  // [K]
+  // Compaction descriptors: for scale t, the kept (l, h) sorted by l; the
+  // ones of layer l are desc_first[t*(L+1)+l] .. desc_first[t*(L+1)+l+1].
+  std::vector<int64_t> desc_first;
+  void* kcache;
+  void* vcache;
+  int64_t* d_base = nullptr;
+  int32_t* d_cap = nullptr;
+  int32_t* d_lenb = nullptr;
+  hk::CopyDesc* d_desc = nullptr;
+  float* d_partials = nullptr;
+  std::vector<int> appended;      // last scale appended per layer (-1: none)
+};
+
+namespace {
+
+using hk::fail;
+
+// Makes the context's device current for the duration of a call.
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HK_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void free_tables(hk_ctx* c) {
+  (void)hipFree(c->d_base);
+  (void)hipFree(c->d_cap);
+  (void)hipFree(c->d_lenb);
+  (void)hipFree(c->d_desc);
+  (void)hipFree(c->d_partials);
+  c->d_base = nullptr;
+  c->d_cap = nullptr;
+  c->d_lenb = nullptr;
+  c->d_desc = nullptr;
+  c->d_partials = nullptr;
+}
+
+// Query rows per attend workgroup.
+int rows_per_workgroup(int dtype) { return dtype == HK_DTYPE_BF16 ? 128 : 64; }
+
+template <typename T>
+hipError_t upload(T** dst, const std::vector<T>& src) {
+  const size_t bytes = std::max<size_t>(src.size(), 1) * sizeof(T);
+  hipError_t e = hipMalloc(reinterpret_cast<void**>(dst), bytes);
+  if (e != hipSuccess) return e;
+  if (src.empty()) return hipSuccess;
+  return hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+int check_step_args(const hk_ctx* c, int layer, int step) {
+  if (!c) return fail(HK_EINVAL, "null context");
+  if (layer < 0 || layer >= c->L) return fail(HK_EINVAL, "layer %d out of [0, %d)", layer, c->L);
+  if (step < 0 || step >= c->K) return fail(HK_EINVAL, "step %d out of [0, %d)", step, c->K);
+  return HK_OK;
+}
+
+int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
+                  const void* v_cur, void* out, float softmax_scale, float* scas_table,
+                  bool scas, void* hip_stream) {
+  int rc = check_step_args(c, layer, step);
+  if (rc != HK_OK) return rc;
+  if (!q || !k_cur || !v_cur || !out) return fail(HK_EINVAL, "null tensor pointer");
+  if (scas && !scas_table) return fail(HK_EINVAL, "null S-CAS table");
+  if (!aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) || !aligned16(out))
+    return fail(HK_EINVAL, "tensor pointers must be 16-byte aligned");
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
+    return fail(HK_EINVAL, "softmax_scale must be positive and finite");
+  if (step > 0 && c->appended[layer] < step - 1)
+    return fail(HK_EORDER, "attend(layer %d, step %d) needs scale %d appended first (last: %d)",
+                layer, step, step - 1, c->appended[layer]);
+
+  DeviceGuard g(c->device);
+  if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+
+  hk::AttendArgs a{};
+  a.q = q;
+  a.kcur = k_cur;
+  a.vcur = v_cur;
+  a.out = out;
+  a.kcache = c->kcache;
+  a.vcache = c->vcache;
+  a.base = c->d_base + int64_t(layer) * c->H;
+  a.cap = c->d_cap + int64_t(layer) * c->H;
+  a.lenb = c->d_lenb + int64_t(layer) * c->H * c->K;
+  a.partials = c->d_partials;
+  a.B = c->B;
+  a.H = c->H;
+  a.n = c->tokens[step];
+  a.K = c->K;
+  a.step = step;
+  a.n_qtiles = (a.n + rows_per_workgroup(c->dtype) - 1) / rows_per_workgroup(c->dtype);
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+
+  hipError_t e = c->dtype == HK_DTYPE_BF16 ? hk::launch_attend_bf16_d128(a, scas, s)
+                                           : hk::launch_attend_f32(a, c->D, scas, s);
+  if (e != hipSuccess) return hip_fail(e, "attend launch");
+  if (scas) {
+    e = hk::launch_scas_finalize(c->d_partials, scas_table, layer, c->H, c->K, c->B, a.n, step,
+                                 a.n_qtiles, s);
+    if (e != hipSuccess) return hip_fail(e, "S-CAS finalize launch");
+  }
+  return HK_OK;
+}
+
+}  // namespace
+
+extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
+                         const int32_t* scale_tokens, const uint8_t* keep, int dtype,
+                         void* k_cache, void* v_cache) {
+  if (!out) return fail(HK_EINVAL, "null output pointer");
+  *out = nullptr;
+  if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
+  if (K > HK_MAX_SCALES) return fail(HK_EUNSUPPORTED, "K = %d exceeds %d scales", K, HK_MAX_SCALES);
+  if (!scale_tokens || !keep) return fail(HK_EINVAL, "null scale_tokens or keep");
+  if (dtype == HK_DTYPE_BF16) {
+    if (D != 128) return fail(HK_EUNSUPPORTED, "bf16 needs head_dim 128 (got %d)", D);
+  } else if (dtype == HK_DTYPE_F32) {
+    if (D != 16 && D != 32 && D != 64 && D != 128)
+      return fail(HK_EUNSUPPORTED, "f32 needs head_dim 16, 32, 64 or 128 (got %d)", D);
+  } else {
+    return fail(HK_EUNSUPPORTED, "unknown dtype %d", dtype);
+  }
+  for (int s = 0; s < K; ++s)
+    if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+
+  auto* c = new hk_ctx();
+  c->L = L; c->H = H; c->D = D; c->B = B; c->K = K; c->dtype = dtype;
+  c->elem_bytes = dtype == HK_DTYPE_BF16 ? 2 : 4;
+  c->tokens.assign(scale_tokens, scale_tokens + K);
+  c->keep.assign(keep, keep + int64_t(L) * H * K);
+  for (auto& v : c->keep) v = v ? 1 : 0;
+  c->kcache = k_cache;
+  c->vcache = v_cache;
+  c->appended.assign(L, -1);
+
+  const int64_t heads = int64_t(L) * H;
+  c->cap.assign(heads, 0);
+  c->base.assign(heads, 0);
+  c->lenb.assign(heads * K, 0);
+  int64_t offset = 0;
+  for (int64_t f = 0; f < heads; ++f) {
+    int64_t run = 0;
+    for (int t = 0; t < K; ++t) {
+      c->lenb[f * K + t] = int32_t(run);
+      if (t <= K - 2 && c->keep[f * K + t]) run += scale_tokens[t];
+    }
+    if (run > INT32_MAX) { delete c; return fail(HK_EINVAL, "head cache exceeds 2^31 rows"); }
+    c->cap[f] = run;
+    c->base[f] = offset;
+    offset += run * B * D;
+  }
+  const int64_t cache_elems = offset;
+  if (cache_elems > 0 && (!k_cache || !v_cache)) {
+    delete c;
+    return fail(HK_EINVAL, "null cache buffer");
+  }
+  if (!aligned16(k_cache) || !aligned16(v_cache)) {
+    delete c;
+    return fail(HK_EINVAL, "cache buffers must be 16-byte aligned");
+  }
+
+  c->retained.assign(K, 0);
+  int64_t run = 0;
+  for (int k = 0; k < K; ++k) {
+    if (k <= K - 2)
+      for (int64_t f = 0; f < heads; ++f) run += c->keep[f * K + k] * int64_t(scale_tokens[k]);
+    c->retained[k] = run;
+  }
+
+  std::vector<hk::CopyDesc> desc;
+  c->desc_first.assign(int64_t(K) * (L + 1), 0);
+  for (int t = 0; t < K; ++t) {
+    for (int l = 0; l < L; ++l) {
+      c->desc_first[int64_t(t) * (L + 1) + l] = int64_t(desc.size());
+      if (t > K - 2) continue;
+      for (int h = 0; h < H; ++h) {
+        const int64_t f = int64_t(l) * H + h;
+        if (!c->keep[f * K + t]) continue;
+        hk::CopyDesc d{};
+        d.dst = (c->base[f] + int64_t(c->lenb[f * K + t]) * D) * c->elem_bytes;
+        d.cap = int32_t(c->cap[f]);
+        d.head = h;
+        d.layer = l;
+        desc.push_back(d);
+      }
+    }
+    c->desc_first[int64_t(t) * (L + 1) + L] = int64_t(desc.size());
+  }
+
+  int64_t max_partials = 1;
+  for (int t = 0; t < K; ++t) {
+    const int64_t qt = (scale_tokens[t] + rows_per_workgroup(dtype) - 1) / rows_per_workgroup(dtype);
+    max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
+  }
+
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = upload(&c->d_base, c->base);
+  std::vector<int32_t> cap32(c->cap.begin(), c->cap.end());
+  if (e == hipSuccess) e = upload(&c->d_cap, cap32);
+  if (e == hipSuccess) e = upload(&c->d_lenb, c->lenb);
+  if (e == hipSuccess) e = upload(&c->d_desc, desc);
+  if (e == hipSuccess)
+    e = hipMalloc(reinterpret_cast<void**>(&c->d_partials),
+                  size_t(max_partials) * hk::kMaxScales * sizeof(float));
+  if (e != hipSuccess) {
+    free_tables(c);
+    delete c;
+    return hip_fail(e, "context tables");
+  }
+  *out = c;
+  return HK_OK;
+}
+
+extern "C" int hk_destroy(hk_ctx* c) {
+  if (!c) return HK_OK;
+  int rc = HK_OK;
+  {
+    DeviceGuard g(c->device);
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = hip_fail(e, "synchronise before destroy");
+    free_tables(c);
+  }
+  delete c;
+  return rc;
+}
+
+extern "C" int hk_reset(hk_ctx* c) {
+  if (!c) return fail(HK_EINVAL, "null context");
+  c->appended.assign(c->L, -1);
+  return HK_OK;
+}
+
+extern "C" int hk_attend(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
+                         const void* v_cur, void* out, float softmax_scale, void* hip_stream) {
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, nullptr, false,
+                       hip_stream);
+}
+
+extern "C" int hk_attend_with_scas(hk_ctx* c, int layer, int step, const void* q,
+                                   const void* k_cur, const void* v_cur, void* out,
+                                   float softmax_scale, float* scas_table, void* hip_stream) {
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, scas_table, true,
+                       hip_stream);
+}
+
+extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int step,
+                               const void* k_cur, const void* v_cur, int64_t layer_stride_elems,
+                               void* hip_stream) {
+  if (!c) return fail(HK_EINVAL, "null context");
+  if (layer_begin < 0 || layer_end > c->L || layer_begin >= layer_end)
+    return fail(HK_EINVAL, "layer range [%d, %d) invalid for %d layers", layer_begin, layer_end, c->L);
+  if (step < 0 || step > c->K - 2)
+    return fail(HK_EINVAL, "step %d cannot be appended (cached scales are 0..%d)", step, c->K - 2);
+  if (!k_cur || !v_cur) return fail(HK_EINVAL, "null tensor pointer");
+  if (!aligned16(k_cur) || !aligned16(v_cur))
+    return fail(HK_EINVAL, "tensor pointers must be 16-byte aligned");
+  const int nl = layer_end - layer_begin;
+  if (nl > 1 && (layer_stride_elems < 0 ||
+                 (layer_stride_elems * c->elem_bytes) % 16 != 0))
+    return fail(HK_EINVAL, "layer stride must be non-negative and a multiple of 16 bytes");
+  for (int l = layer_begin; l < layer_end; ++l)
+    if (c->appended[l] != step - 1)
+      return fail(HK_EORDER, "append(layer %d, step %d) out of order (last appended: %d)", l,
+                  step, c->appended[l]);
+
+  const int64_t first = c->desc_first[int64_t(step) * (c->L + 1) + layer_begin];
+  const int64_t last = c->desc_first[int64_t(step) * (c->L + 1) + layer_end];
+  if (last > first) {
+    DeviceGuard g(c->device);
+    if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+    hk::CompactArgs a{};
+    a.desc = c->d_desc + first;
+    a.kcur = static_cast<const uint8_t*>(k_cur);
+    a.vcur = static_cast<const uint8_t*>(v_cur);
+    a.kcache = static_cast<uint8_t*>(c->kcache);
+    a.vcache = static_cast<uint8_t*>(c->vcache);
+    a.layer_stride_bytes = nl > 1 ? layer_stride_elems * c->elem_bytes : 0;
+    a.n_desc = int(last - first);
+    a.B = c->B;
+    a.n = c->tokens[step];
+    a.H = c->H;
+    a.row_bytes = c->D * c->elem_bytes;
+    // 1024 16-byte vectors per tensor per workgroup: 4 per lane.
+    a.rows_per_block = std::min(std::max(1, 16384 / a.row_bytes), a.n);
+    a.chunks = (a.n + a.rows_per_block - 1) / a.rows_per_block;
+    a.layer_begin = layer_begin;
+    hipError_t e = hk::launch_compact(a, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
+  }
+  for (int l = layer_begin; l < layer_end; ++l) c->appended[l] = step;
+  return HK_OK;
+}
+
+extern "C" int hk_retained_tokens(const hk_ctx* c, int step, int64_t* out) {
+  if (!c || !out) return fail(HK_EINVAL, "null argument");
+  if (step < 0 || step >= c->K) return fail(HK_EINVAL, "step %d out of [0, %d)", step, c->K);
+  *out = c->retained[step];
+  return HK_OK;
+}

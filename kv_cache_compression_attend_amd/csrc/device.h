@@ -1,0 +1,70 @@
+// Device-side types and launch descriptors shared by the kernels and the
+// host launch code.  gfx950 (CDNA4) only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hk {
+
+constexpr int kMaxScales = 16;   // S-CAS accumulators per query row
+constexpr int kXcds = 8;         // MI355X: 8 accelerator dies, 32 CUs each
+
+// Arguments of one attend launch: one layer, one scale step.
+struct AttendArgs {
+  const void* q;          // [B][n][H][D]
+  const void* kcur;       // [B][n][H][D]
+  const void* vcur;       // [B][n][H][D]
+  void* out;              // [B][n][H][D]
+  const void* kcache;     // whole K cache buffer
+  const void* vcache;     // whole V cache buffer
+  const int64_t* base;    // [H] element offset of head (layer, h)
+  const int32_t* cap;     // [H] cache rows per batch entry of head (layer, h)
+  const int32_t* lenb;    // [H][K] rows cached before each scale
+  float* partials;        // S-CAS partial sums [B*H*n_qtiles][kMaxScales]
+  int B, H, n, K, step, n_qtiles;
+  float scale;            // softmax scale alpha
+  float scale_log2;       // alpha * log2(e)
+};
+
+// One kept (layer, head) segment of a completed scale, to be copied into the cache.
+struct CopyDesc {
+  int64_t dst;            // byte offset of row len_before(l,h,t) of (l,h,b=0)
+  int32_t cap;            // rows per batch entry of (l,h)
+  int32_t head;
+  int32_t layer;
+  int32_t pad;
+};
+
+struct CompactArgs {
+  const CopyDesc* desc;   // descriptors of this launch
+  const uint8_t* kcur;    // byte views
+  const uint8_t* vcur;
+  uint8_t* kcache;
+  uint8_t* vcache;
+  int64_t layer_stride_bytes;
+  int n_desc, B, n, H;
+  int layer_begin;        // layer whose tensor starts at kcur / vcur
+  int row_bytes;          // D * element size, a multiple of 16
+  int rows_per_block;
+  int chunks;             // row blocks per (desc, b)
+};
+
+// Workgroups are handed to the 8 dies round-robin (workgroup i runs on die
+// i % 8).  This maps the hardware index to a logical index so that each die
+// receives one contiguous range of logical work, keeping a head's query tiles
+// (which read the same keys and values) on one die and its L2.
+__device__ __forceinline__ int xcd_logical(int i, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int x = i % kXcds, k = i / kXcds;
+  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+// Launchers (defined next to their kernels).
+hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s);
+hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
+hipError_t launch_scas_finalize(const float* partials, float* table, int layer, int H, int K,
+                                int B, int n, int step, int n_qtiles, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+}  // namespace hk

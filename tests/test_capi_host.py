@@ -1,0 +1,133 @@
+"""The C-ABI library on the host (no GPU work): exports, schedule, layout, errors."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads
+from oracle import cache as ocache
+from oracle import schedule as osch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "heatkv.h")
+LIB = os.path.join(ROOT, "kv_cache_compression_attend_amd", "libheatkv.so")
+
+if not os.path.exists(LIB):  # build only when nothing is built
+    from kv_cache_compression_attend_amd import build as _build
+    _build.build()
+
+import kv_cache_compression_attend_amd as hk  # noqa: E402
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hk_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 10, names
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_single_hip_runtime_loaded():
+    maps = open("/proc/self/maps").read()
+    paths = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(paths) == 1, paths
+
+
+def _same_as_oracle(table, tokens, beta, n_sink):
+    try:
+        want = osch.build_schedule(table, tokens, beta, n_sink)
+    except osch.ScheduleError as e:
+        with pytest.raises(hk.HeatKVError) as got:
+            hk.build_schedule(table, tokens, beta, n_sink)
+        assert got.value.name == e.code.upper()
+        return None
+    keep, ret, n = hk.build_schedule(table, tokens, beta, n_sink)
+    np.testing.assert_array_equal(keep, want[0])
+    np.testing.assert_array_equal(ret, want[1])
+    assert n == want[2]
+    return keep
+
+
+@pytest.mark.parametrize("key", ["c0", "c1", "c2", "c3", "c4"])
+def test_schedule_bit_exact_on_workload_tables(key):
+    wl = workloads.get(key)
+    table = workloads.dirichlet_scas(wl)
+    for beta in (wl.budget, 0.2, 0.1, 0.04, 1.0):
+        _same_as_oracle(table, wl.scale_tokens, beta, wl.n_sink)
+
+
+def test_schedule_bit_exact_random_tables():
+    g = np.random.default_rng(7)
+    for i in range(1000):
+        L, H, K = int(g.integers(1, 4)), int(g.integers(1, 6)), int(g.integers(1, 9))
+        tokens = workloads.random_tokens(K, i, max_side=5)
+        table = workloads.random_scas_table(L, H, K, i)
+        if i % 7 == 0:  # plant exact ties
+            table[:, :, :, :] = np.round(table * 4) / 4
+        beta = float(g.choice([g.uniform(0.01, 1.0), 1.0, 0.5]))
+        n_sink = int(g.integers(0, K))
+        _same_as_oracle(table, tokens, beta, n_sink)
+
+
+def test_schedule_errors():
+    t = workloads.random_scas_table(1, 2, 4, 3)
+    tok = (1, 4, 9, 16)
+    for beta, ns in ((0.0, 1), (1.5, 1), (0.5, 4), (0.5, -1), (float("nan"), 1)):
+        with pytest.raises(hk.HeatKVError) as e:
+            hk.build_schedule(t, tok, beta, ns)
+        assert e.value.status == hk.HK_EINVAL
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.build_schedule(t, (1, 0, 9, 16), 0.5, 1)
+    assert e.value.status == hk.HK_EINVAL
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.build_schedule(t, tok, 0.01, 1)
+    assert e.value.status == hk.HK_EBUDGET
+    assert "sink" in hk._lib.hk_last_error().decode()
+
+
+@pytest.mark.parametrize("key", ["c0", "c2", "c4"])
+def test_layout_matches_oracle(key):
+    wl = workloads.get(key)
+    if wl.schedule == "random_drop2":
+        keep = workloads.random_drop2_keep(wl)
+    else:
+        keep = osch.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, wl.budget,
+                                   wl.n_sink)[0]
+    elems, cap, base = hk.layout(wl.scale_tokens, keep, wl.batch, wl.head_dim)
+    ocap = ocache.capacity(keep, wl.scale_tokens)
+    np.testing.assert_array_equal(cap, ocap)
+    np.testing.assert_array_equal(base, ocache.bases(ocap, wl.batch, wl.head_dim))
+    assert elems * (2 if wl.dtype == "bf16" else 4) == ocache.cache_bytes(
+        keep, wl.scale_tokens, wl.batch, wl.head_dim, 2 if wl.dtype == "bf16" else 4)
+
+
+def test_null_and_range_errors_without_gpu():
+    lib = hk._lib
+    assert lib.hk_attend(None, 0, 0, None, None, None, None, 1.0, None) == hk.HK_EINVAL
+    assert lib.hk_append_scale(None, 0, 1, 0, None, None, 0, None) == hk.HK_EINVAL
+    assert lib.hk_reset(None) == hk.HK_EINVAL
+    assert lib.hk_destroy(None) == hk.HK_OK
+    out = ctypes.c_int64()
+    assert lib.hk_retained_tokens(None, 0, ctypes.byref(out)) == hk.HK_EINVAL
+    tok = np.array([1, 4], dtype=np.int32)
+    keep = np.ones((1, 1, 2), dtype=np.uint8)
+    h = ctypes.c_void_p()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    assert lib.hk_create(ctypes.byref(h), 1, 1, 64, 1, 2, p(tok), p(keep), hk.HK_DTYPE_BF16,
+                         None, None) == hk.HK_EUNSUPPORTED
+    assert lib.hk_create(ctypes.byref(h), 1, 1, 128, 1, 17, p(np.ones(17, np.int32)),
+                         p(np.ones(17, np.uint8)), hk.HK_DTYPE_BF16, None, None) == hk.HK_EUNSUPPORTED
+    assert lib.hk_create(ctypes.byref(h), 1, 1, 24, 1, 2, p(tok), p(keep), hk.HK_DTYPE_F32,
+                         None, None) == hk.HK_EUNSUPPORTED
+    assert lib.hk_create(ctypes.byref(h), 0, 1, 16, 1, 2, p(tok), p(keep), hk.HK_DTYPE_F32,
+                         None, None) == hk.HK_EINVAL
+    assert lib.hk_create(ctypes.byref(h), 1, 1, 16, 1, 2, p(tok), p(keep), hk.HK_DTYPE_F32,
+                         None, None) == hk.HK_EINVAL  # null cache with a non-empty layout

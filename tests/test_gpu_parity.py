@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerances: bf16 attention output max-abs <= 1e-2 and mean-abs <= 1e-3;
+fp32 attention output max-abs <= 1e-5; S-CAS <= 1e-4 absolute; keep-masks
+and compacted caches bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import schedule as osch
+from oracle.numerics import to_f64
+
+import kv_cache_compression_attend_amd as hk
+from _gpu import (check_cache, generate, gpu_rows, note, oracle_rows, sample_rows, to_device,
+                  torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX, BF16_MEAN, F32_MAX, SCAS_TOL = 1e-2, 1e-3, 1e-5, 1e-4
+
+
+def _tol(wl):
+    return (BF16_MAX, BF16_MEAN) if wl.dtype == "bf16" else (F32_MAX, F32_MAX)
+
+
+def _compare_outputs(run, layers, rows_per_unit=96, bh=None, seed=0):
+    wl = run.wl
+    tmax, tmean = _tol(wl)
+    worst = 0.0
+    for l in layers:
+        for t in range(wl.n_scales):
+            n = wl.scale_tokens[t]
+            rows = sample_rows(n, rows_per_unit, seed + 31 * t + l)
+            pairs = bh if bh is not None else [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+            err_sum, err_cnt = 0.0, 0
+            for b, h in pairs:
+                want, _ = oracle_rows(run, l, t, b, h, rows)
+                got = gpu_rows(run, l, t, b, h, rows)
+                assert np.isfinite(got).all(), (l, t, b, h)
+                e = np.abs(got - want)
+                worst = max(worst, float(e.max()))
+                assert e.max() <= tmax, (l, t, b, h, float(e.max()))
+                err_sum += float(e.sum())
+                err_cnt += e.size
+            assert err_sum / err_cnt <= tmean, (l, t, err_sum / err_cnt)
+    return worst
+
+
+def _compare_scas(run, l, steps=None, heads=None, tol=SCAS_TOL):
+    wl = run.wl
+    steps = range(wl.n_scales) if steps is None else steps
+    heads = range(wl.heads) if heads is None else heads
+    for t in steps:
+        rows = np.arange(wl.scale_tokens[t])
+        for h in heads:
+            mass = np.zeros(t + 1)
+            for b in range(wl.batch):
+                _, m = oracle_rows(run, l, t, b, h, rows)
+                mass += m
+            mass /= wl.batch
+            got = run.scas[l, h, t, : t + 1].astype(np.float64)
+            np.testing.assert_allclose(got, mass, atol=tol, rtol=0, err_msg=f"l{l} h{h} t{t}")
+            for s in range(t):
+                if not run.keep[l, h, s]:
+                    assert run.scas[l, h, t, s] == 0.0
+            assert (run.scas[l, h, t, t + 1:] == 0).all()
+
+
+def _schedule(wl):
+    if wl.schedule == "random_drop2":
+        return workloads.random_drop2_keep(wl)
+    if wl.schedule == "full":
+        keep, _, n = hk.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, 1.0, wl.n_sink)
+        assert n == 0
+        return keep
+    table = workloads.dirichlet_scas(wl)
+    keep, ret, n = hk.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
+    want = osch.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
+    np.testing.assert_array_equal(keep, want[0])
+    return keep
+
+
+def _custom(index, name, sides, heads, head_dim, batch, dtype, layers=1, alpha=None):
+    return workloads.Workload(
+        index=index, name=name, layers=layers, heads=heads, head_dim=head_dim, batch=batch,
+        sides=tuple(sides), dtype=dtype, budget=1.0, n_sink=1,
+        softmax_scale=alpha if alpha is not None else (1.0 if dtype == "bf16" else head_dim ** -0.5),
+        qk_std=head_dim ** -0.25 if dtype == "bf16" else 1.0, schedule="custom")
+
+
+def _random_keep(wl, seed, p=0.5):
+    g = np.random.default_rng(seed)
+    keep = (g.random((wl.layers, wl.heads, wl.n_scales)) < p).astype(np.uint8)
+    keep[:, :, 0] = 1
+    keep[:, :, -1] = 0
+    keep[0, 0, 1:] = 0  # one head keeps only the sink
+    return keep
+
+
+def test_tiny_f32_workload():
+    wl = workloads.get("c0")
+    keep = _schedule(wl)
+    run = generate(wl, keep, [0], scas=True)
+    _compare_outputs(run, [0])
+    _compare_scas(run, 0, tol=1e-5)
+    check_cache(run, [0])
+    run.ctx.close()
+
+
+def test_infinity2b_layer_full_cache():
+    wl = workloads.get("c1")
+    keep = _schedule(wl)
+    run = generate(wl, keep, [0])
+    worst = _compare_outputs(run, [0])
+    note(f"c1 worst max-abs {worst:.3e}")
+    check_cache(run, [0])
+    run.ctx.close()
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_f32_head_dims_ragged(D):
+    wl = _custom(20 + D, f"ragged-f32-d{D}", (1, 3, 5, 7, 9), heads=3, head_dim=D, batch=2,
+                 dtype="f32", layers=2)
+    keep = _random_keep(wl, D)
+    run = generate(wl, keep, [0, 1], scas=True, multi_layer_append=True)
+    _compare_outputs(run, [0, 1])
+    for l in (0, 1):
+        _compare_scas(run, l, tol=1e-5)
+    check_cache(run, [0, 1])
+    run.ctx.close()
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bf16_ragged_tiles_and_junctions(seed):
+    """Scale sizes that are not multiples of the 128-query / 64-key tiles, cache
+    lengths that end mid-tile, heads that keep nothing but the sink."""
+    wl = _custom(30 + seed, f"ragged-bf16-{seed}", (1, 3, 5, 7, 11, 13, 17, 19, 23), heads=5,
+                 head_dim=128, batch=3, dtype="bf16", layers=3)
+    keep = _random_keep(wl, 100 + seed)
+    run = generate(wl, keep, [0, 1, 2], scas=True, multi_layer_append=bool(seed))
+    _compare_outputs(run, [0, 1, 2], rows_per_unit=400)
+    for l in range(3):
+        _compare_scas(run, l)
+    check_cache(run, [0, 1, 2])
+    run.ctx.close()
+
+
+def test_single_scale_workload():
+    wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
+    keep = np.zeros((1, 2, 1), dtype=np.uint8)
+    run = generate(wl, keep, [0], scas=True)
+    _compare_outputs(run, [0])
+    _compare_scas(run, 0)
+    run.ctx.close()
+
+
+def test_pruned_10pct_full_size_layers():
+    """32 layers x 16 heads, batch 8, 10% budget; two layers run end to end."""
+    wl = workloads.get("c2")
+    keep = _schedule(wl)
+    layers = [0, 13]
+    run = generate(wl, keep, layers)
+    pairs = [(b, h) for b in (0, 3, 7) for h in range(16)]
+    _compare_outputs(run, layers, rows_per_unit=48, bh=pairs)
+    check_cache(run, layers)
+    run.ctx.close()
+
+
+def test_calibration_full_size_scas():
+    """32 x 16 heads, batch 4, full cache, S-CAS on; key offsets make rankings non-uniform."""
+    wl = workloads.get("c3")
+    keep = _schedule(wl)
+    run = generate(wl, keep, [0], scas=True)
+    pairs = [(b, h) for b in range(4) for h in (0, 5, 10, 15)]
+    _compare_outputs(run, [0], rows_per_unit=48, bh=pairs)
+    _compare_scas(run, 0, steps=range(10))
+    _compare_scas(run, 0, steps=(10, 11, 12), heads=(0, 9))
+    table = run.scas[0]
+    for t in range(wl.n_scales):
+        np.testing.assert_allclose(table[:, t, : t + 1].sum(axis=1), 1.0, atol=1e-4)
+    run.ctx.close()
+
+
+def test_infinity8b_shape_4pct_layer():
+    """40 layers x 28 heads, batch 16, 4% budget; one layer end to end."""
+    wl = workloads.get("c4")
+    keep = _schedule(wl)
+    run = generate(wl, keep, [7])
+    pairs = [(b, h) for b in (0, 15) for h in range(28)]
+    _compare_outputs(run, [7], rows_per_unit=32, bh=pairs)
+    check_cache(run, [7])
+    run.ctx.close()
+
+
+def test_determinism_and_scas_repeat():
+    wl = workloads.get("c1")
+    keep = _schedule(wl)
+    ctx = hk.Context(1, 16, 128, 1, wl.scale_tokens, keep, torch.bfloat16)
+    table = torch.zeros((1, 16, 13, 13), dtype=torch.float32, device="cuda")
+    outs = []
+    for rep in range(2):
+        ctx.reset()
+        got = []
+        for t in range(13):
+            inp = workloads.step_inputs(wl, 0, t)
+            q, k, v = to_device(inp.q, wl), to_device(inp.k, wl), to_device(inp.v, wl)
+            out = torch.empty_like(q)
+            note(f"determinism rep {rep} step {t}")
+            ctx.attend_with_scas(0, t, q, k, v, out, 1.0, table)
+            got.append(out.view(torch.int16).cpu().numpy())
+            if t < 12:
+                ctx.append_scale(0, 1, t, k, v)
+        got.append(table.cpu().numpy().view(np.int32))
+        outs.append(got)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    ctx.close()
+
+
+def test_order_and_argument_errors():
+    wl = _custom(50, "errors", (1, 2, 3), heads=2, head_dim=128, batch=1, dtype="bf16")
+    keep = np.ones((1, 2, 3), dtype=np.uint8)
+    ctx = hk.Context(1, 2, 128, 1, wl.scale_tokens, keep, torch.bfloat16)
+    mk = lambda t: torch.zeros((1, wl.scale_tokens[t], 2, 128), dtype=torch.bfloat16, device="cuda")  # noqa
+    with pytest.raises(hk.HeatKVError) as e:
+        ctx.attend(0, 1, mk(1), mk(1), mk(1), mk(1), 1.0)
+    assert e.value.status == hk.HK_EORDER
+    with pytest.raises(hk.HeatKVError) as e:
+        ctx.append_scale(0, 1, 1, mk(1), mk(1))
+    assert e.value.status == hk.HK_EORDER
+    with pytest.raises(hk.HeatKVError) as e:
+        ctx.append_scale(0, 1, 2, mk(2), mk(2))
+    assert e.value.status == hk.HK_EINVAL
+    with pytest.raises(hk.HeatKVError) as e:
+        ctx.attend(0, 0, mk(1), mk(0), mk(0), mk(0), 1.0)   # wrong shape
+    assert e.value.status == hk.HK_EINVAL
+    with pytest.raises(hk.HeatKVError) as e:
+        ctx.attend(0, 0, mk(0), mk(0), mk(0), mk(0), -1.0)
+    assert e.value.status == hk.HK_EINVAL
+    # raw ABI: misaligned pointer is rejected before any launch
+    base = mk(2)
+    p = base.data_ptr() + 2
+    import ctypes
+    rc = hk._lib.hk_attend(ctx._h, 0, 0, ctypes.c_void_p(p), ctypes.c_void_p(p),
+                           ctypes.c_void_p(p), ctypes.c_void_p(p), 1.0, None)
+    assert rc == hk.HK_EINVAL
+    ctx.attend(0, 0, mk(0), mk(0), mk(0), mk(0), 1.0)
+    ctx.append_scale(0, 1, 0, mk(0), mk(0))
+    assert ctx.retained_tokens(0) == 2 and ctx.retained_tokens(2) == 2 * (1 + 4)
+    torch.cuda.synchronize()
+    ctx.close()

@@ -54,7 +54,9 @@ def parse():
     ap.add_argument("--no-pruned", action="store_true",
                     help="skip the 32-layer 10%%-budget scales/s measurement")
     ap.add_argument("--pruned-steps", type=int, default=5)
-    ap.add_argument("--cpu-heads", type=int, default=4,
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
+    ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
     return ap.parse_args()
 
@@ -108,6 +110,14 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each": src.numel() * 2, "copies": 3}), flush=True)
+        return
 
     # ---------------- main workload: one full-cache Infinity-2B-shaped layer ----------------
     wl = workloads.get("c1")

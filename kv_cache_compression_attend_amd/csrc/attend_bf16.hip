@@ -8,31 +8,52 @@
 // caption).  With S-CAS on, it also accumulates the probability mass each
 // query puts on each source scale (HeatKV project page, Method step 2).
 //
-// Design (one workgroup = 4 waves = 128 queries of one (batch, head)):
+// Shared design:
 //   * Scores are computed transposed, S^T = K Q^T, with
-//     v_mfma_f32_32x32x16_bf16: each lane then owns one query column and 16
-//     key rows per 32x32 block, so a query's running max and sum stay in the
-//     lane (one exchange with the lane 32 apart per key tile).
+//     v_mfma_f32_32x32x16_bf16: each lane owns one query column and 16 key
+//     rows per 32x32 block, so a query's max and sum stay in the lane (one
+//     exchange with the lane 32 apart per 32 keys).
 //   * The key rows fed to the score product are permuted (bits 2 and 3 of the
-//     row index swapped) so that the score accumulator of each lane already
-//     holds, for every 16-key step of the value product, the 8 consecutive
-//     keys the B operand of O^T = V^T P^T needs: probabilities go from the
-//     score registers straight into the value product, without LDS.
+//     row index swapped) so that each lane's score registers already hold,
+//     for every 16-key step of the value product, the 8 consecutive keys the
+//     B operand of O^T = V^T P^T needs: probabilities go from the score
+//     registers straight into the value product.
 //   * K tiles are staged row-major in LDS; V tiles are transposed on the way
 //     in (4 keys x 8 dims per lane, repacked in registers) so the A operand
 //     of the value product is one 16-byte LDS read.  Row strides are padded
-//     so both the staging writes and the operand reads are free of bank
-//     conflicts.
-//   * The next tile's global loads are issued before the current tile is
-//     computed; the key index selects the source row: the cache for the
-//     first len_before keys, the current scale's K/V rows after that, so the
-//     junction needs no padding.
-//   * fp32 online softmax in base 2 (alpha * log2 e folded into one multiply).
-//   * S-CAS: per-lane fp32 accumulators for up to 16 source scales, rescaled
-//     with the running max, reduced across the workgroup and written as one
-//     partial row per workgroup; a second kernel sums the partials in a fixed
-//     order (no float atomics, deterministic).
+//     so the operand reads are free of bank conflicts.
+//   * Global loads are buffer loads from per-tile scalar descriptors whose
+//     size ends at the last valid row, so rows past the end read as zero and
+//     the per-lane offsets stay constant.  A 64-key tile lies in the cache,
+//     in the current scale, or (at most once) across the junction, where each
+//     row picks its source; the junction needs no padding.
+//   * fp32 online softmax in base 2 (alpha * log2 e folded into one fma).
+//     The running max is raised only when a block's max exceeds it by more
+//     than 2^8, so the output accumulators are rescaled on a few blocks
+//     rather than on every one; probabilities stay below 256, which bf16 and
+//     fp32 hold as precisely as values below 1.
+//   * Without S-CAS the softmax denominator is summed from the same bf16
+//     probabilities the value product uses (v_dot2 against ones: half the
+//     adds).  With S-CAS it is summed in fp32 together with per-source
+//     accumulators, rescaled with the running max, reduced across the
+//     workgroup into one partial row per workgroup; a second kernel adds the
+//     partials in a fixed order (no float atomics, deterministic).
+//
+// Two tilings:
+//   * 128 queries per workgroup of 4 waves, two workgroups per CU; the 64-key
+//     tile is scored, normalised and accumulated in sequence.  Used when the
+//     launch is too small to fill the chip with 256-query workgroups.
+//   * 256 queries per workgroup of 8 waves (two per SIMD).  Per 32-key unit u
+//     a wave runs the score product QK(u) (8 MFMAs), the softmax SM(u) and
+//     the value product PV(u) (8 MFMAs), pipelined as step
+//     i = { PV(u_{i-1}), QK(u_{i+1}) } on the matrix cores beside SM(u_i) on
+//     the vector ALUs.  K tiles are staged one tile ahead of V tiles (waves
+//     4-7 load K, waves 0-3 load V) in three LDS buffers each, one barrier
+//     per 64 keys.  The first and last tiles are separate instantiations, so
+//     the steady-state step is straight-line code.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device.h"
 
@@ -41,17 +62,23 @@ namespace hk {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;        // head_dim
-constexpr int BM = 128;       // queries per workgroup
-constexpr int BN = 64;        // keys per tile
+constexpr int BN = 64;        // keys per staged tile
 constexpr int KSTR = D + 8;   // K tile row stride (bf16 elements): 272 bytes
 constexpr int VSTR = BN + 8;  // V^T tile row stride (bf16 elements): 144 bytes
-constexpr int kThreads = 256;
+constexpr int kRowBytes = D * 2;
+constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr unsigned kOutOfRange = 0x80000000u;
+constexpr int kRsrcFlags = 0x00020000;
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
 union Vec16 {
-  uint4 u;
+  u32x4 u;
   bf16x8 b;
   uint32_t w[4];
 };
@@ -61,152 +88,288 @@ __device__ __forceinline__ int permuted_row(int i) {
   return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = __bf16(lo), b = __bf16(hi);
-  return uint32_t(__builtin_bit_cast(uint16_t, a)) |
-         (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+// Key (within a 32-key block) held in score register v of a lane in half hf.
+__device__ __forceinline__ int key_of(int v, int hf) {
+  const int kp = v >> 2, r = v & 3;
+  return 16 * (kp >> 1) + 8 * hf + 4 * (kp & 1) + r;
 }
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2 f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// acc + lo(w) + hi(w), the two bf16 halves of w summed in fp32.
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                         __builtin_bit_cast(bf16x2, kOnesBf16x2), acc, false);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int nrec = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : int(bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, nrec, kRsrcFlags);
+}
+
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+}
+
+// Where the keys (or values) of one (batch, head) live: cache rows [0, Lc),
+// then the current scale's rows; Ltot keys in all.
+struct KeySource {
+  const char* cache;  // row r at cache + r * kRowBytes
+  const char* cur;    // row r at cur + r * tokb
+  int Lc, Ltot, n, tokb;
+};
+
+// Four 16-byte vectors of the 64-row tile starting at key k0: rows
+// r0 + rstep * i (i = 0..3), 16-byte chunk c.  Rows past the end read 0.
+__device__ __forceinline__ void load_rows(const KeySource& s, int k0, int r0, int rstep, int c,
+                                          u32x4 (&reg)[4]) {
+  if (k0 + BN <= s.Lc) {  // all rows in the cache
+    const auto r = rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reg[i] = bload(r, unsigned(r0 + rstep * i) * kRowBytes + 16u * c);
+  } else if (k0 >= s.Lc) {  // all rows in the current scale
+    const int64_t q0 = k0 - s.Lc;
+    const auto r = rsrc(s.cur + q0 * s.tokb, int64_t(s.n - q0 - 1) * s.tokb + kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reg[i] = bload(r, unsigned(r0 + rstep * i) * s.tokb + 16u * c);
+  } else {  // junction: rows below split from the cache, the rest from the current scale
+    const int split = s.Lc - k0;
+    const auto rc = rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
+    const auto ru = rsrc(s.cur - int64_t(split) * s.tokb, int64_t(split + s.n - 1) * s.tokb + kRowBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + rstep * i;
+      const unsigned oc = row < split ? unsigned(row) * kRowBytes + 16u * c : kOutOfRange;
+      const unsigned ou = row >= split ? unsigned(row) * s.tokb + 16u * c : kOutOfRange;
+      reg[i] = bload(rc, oc) | bload(ru, ou);
+    }
+  }
+}
+
+// K staging over 256 lanes: lane l holds chunk l & 15 of rows (l >> 4) + 16 i.
+__device__ __forceinline__ void load_k(const KeySource& s, int k0, int l, u32x4 (&reg)[4]) {
+  load_rows(s, k0, l >> 4, 16, l & 15, reg);
+}
+__device__ __forceinline__ void store_k(uint16_t* sK, int l, const u32x4 (&reg)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<u32x4*>(&sK[((l >> 4) + 16 * i) * KSTR + 8 * (l & 15)]) = reg[i];
+}
+
+// V staging over 256 lanes: lane l holds chunk l >> 4 of rows 4 (l & 15) + r,
+// written transposed (dims x keys).
+__device__ __forceinline__ void load_v(const KeySource& s, int k0, int l, u32x4 (&reg)[4]) {
+  load_rows(s, k0, 4 * (l & 15), 1, l >> 4, reg);
+}
+__device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[4]) {
+  const int g = l & 15, c = l >> 4;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a0 = reg[0][w], a1 = reg[1][w], a2 = reg[2][w], a3 = reg[3][w];
+    uint2 even, odd;
+    even.x = (a0 & 0xFFFFu) | (a1 << 16);
+    even.y = (a2 & 0xFFFFu) | (a3 << 16);
+    odd.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
+    odd.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
+    const int d = 8 * c + 2 * w;
+    *reinterpret_cast<uint2*>(&sV[d * VSTR + 4 * g]) = even;
+    *reinterpret_cast<uint2*>(&sV[(d + 1) * VSTR + 4 * g]) = odd;
+  }
+}
+
+// Per-workgroup setup shared by both tilings.
+struct Head {
+  KeySource ks, vs;
+  const char* q;      // (b, row 0, h) of the query tensor
+  int n, tokb, Lc, Ltot, h, b, qt;
+  const int32_t* lenb;
+};
+
+__device__ __forceinline__ Head setup(const AttendArgs& a) {
+  Head hd;
+  const int wg = xcd_logical(blockIdx.x, gridDim.x);
+  hd.qt = wg % a.n_qtiles;
+  const int bh = wg / a.n_qtiles;
+  hd.h = bh % a.H;
+  hd.b = bh / a.H;
+  hd.n = a.n;
+  const int64_t tok = int64_t(a.H) * D;
+  hd.tokb = int(tok * 2);
+  const int cap = a.cap[hd.h];
+  const int64_t hb = (a.base[hd.h] + int64_t(hd.b) * cap * D) * 2;
+  hd.lenb = a.lenb + hd.h * a.K;
+  hd.Lc = hd.lenb[a.step];
+  hd.Ltot = hd.Lc + hd.n;
+  const int64_t curoff = (int64_t(hd.b) * hd.n * tok + hd.h * D) * 2;
+  hd.ks = KeySource{static_cast<const char*>(a.kcache) + hb, static_cast<const char*>(a.kcur) + curoff,
+                    hd.Lc, hd.Ltot, hd.n, hd.tokb};
+  hd.vs = KeySource{static_cast<const char*>(a.vcache) + hb, static_cast<const char*>(a.vcur) + curoff,
+                    hd.Lc, hd.Ltot, hd.n, hd.tokb};
+  hd.q = static_cast<const char*>(a.q) + curoff;
+  return hd;
+}
+
+// Q^T fragments of query qrow: dims 16*kk + 8*hf + [0, 8); zero past the end.
+__device__ __forceinline__ void load_q(const Head& hd, int qrow, int hf, Vec16 (&qf)[8]) {
+  const auto rq = rsrc(hd.q, int64_t(hd.n - 1) * hd.tokb + kRowBytes);
+  const unsigned off = qrow < hd.n ? unsigned(qrow) * unsigned(hd.tokb) + 16u * hf : kOutOfRange;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) qf[kk].u = bload(rq, off + 32u * kk);
+}
+
+// out[b][qrow][h][:] = O / l, bf16.
+__device__ __forceinline__ void store_out(const AttendArgs& a, const Head& hd, int qrow, int hf,
+                                          const f32x16 (&o)[4], float inv) {
+  if (qrow >= hd.n) return;
+  uint16_t* op = static_cast<uint16_t*>(a.out) +
+                 (int64_t(hd.b) * hd.n + qrow) * (int64_t(a.H) * D) + hd.h * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const int d = 32 * db + 8 * kp + 4 * hf;
+      uint2 w;
+      w.x = pack_bf16x2(o[db][4 * kp + 0] * inv, o[db][4 * kp + 1] * inv);
+      w.y = pack_bf16x2(o[db][4 * kp + 2] * inv, o[db][4 * kp + 3] * inv);
+      *reinterpret_cast<uint2*>(op + d) = w;
+    }
+}
+
+// Adds this lane's probabilities of keys [kblk, kblk + 32) to the
+// accumulator of every source segment they fall in.  Source src < step
+// covers cache rows [lenb[src], lenb[src+1]); the current scale covers
+// [Lc, Ltot).  Bounds are wave-uniform scalar loads.
+__device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, int hf,
+                                         const f32x16& p, float psum, int kblk,
+                                         float (&sc)[kMaxScales]) {
+#pragma unroll
+  for (int src = 0; src < kMaxScales; ++src) {
+    if (src > a.step) break;
+    const int lo = hd.lenb[src];
+    const int hi = src < a.step ? hd.lenb[src + 1] : hd.Ltot;
+    if (lo < hi && lo < kblk + 32 && hi > kblk) {
+      float acc = 0.f;
+      if (lo <= kblk && hi >= kblk + 32) {
+        acc = psum;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kblk + key_of(v, hf);
+          acc += (key >= lo && key < hi) ? p[v] : 0.f;
+        }
+      }
+      sc[src] += acc;
+    }
+  }
+}
+
+// Sums each source's normalised mass over the workgroup's valid queries and
+// writes the workgroup's partial row.
+template <int WAVES>
+__device__ __forceinline__ void scas_reduce(const AttendArgs& a, const Head& hd, int qrow,
+                                            float inv, const float (&sc)[kMaxScales],
+                                            float* sRed) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int src = 0; src < kMaxScales; ++src) {
+    float m = (sc[src] + __shfl_xor(sc[src], 32)) * inv;
+    m = qrow < hd.n ? m : 0.f;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m += __shfl_xor(m, off);
+    if (lane == 0) sRed[wave * kMaxScales + src] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x < kMaxScales) {
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) tot += sRed[w * kMaxScales + threadIdx.x];
+    const int64_t row = (int64_t(hd.b) * a.H + hd.h) * a.n_qtiles + hd.qt;
+    a.partials[row * kMaxScales + threadIdx.x] = tot;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128 queries per workgroup, 32 per wave, two workgroups per CU.
+// ---------------------------------------------------------------------------
+// With S-CAS the per-lane source accumulators do not fit beside the rest in
+// 256 registers, so that variant runs one wave per SIMD instead of spilling.
 template <bool SCAS>
-__global__ __launch_bounds__(kThreads, 2) void attend_bf16_d128_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VSTR];
+__global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VSTR];
   __shared__ float sRed[SCAS ? 4 * kMaxScales : 1];
 
-  const int wg = xcd_logical(blockIdx.x, gridDim.x);
-  const int qt = wg % a.n_qtiles;
-  const int bh = wg / a.n_qtiles;
-  const int h = bh % a.H;
-  const int b = bh / a.H;
-
+  const Head hd = setup(a);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
-
-  const int n = a.n;
-  const int64_t tok = int64_t(a.H) * D;  // elements between consecutive tokens
-  const uint16_t* q = static_cast<const uint16_t*>(a.q);
-  const uint16_t* kcur = static_cast<const uint16_t*>(a.kcur) + int64_t(b) * n * tok + h * D;
-  const uint16_t* vcur = static_cast<const uint16_t*>(a.vcur) + int64_t(b) * n * tok + h * D;
-  const int cap = a.cap[h];
-  const int64_t hb = a.base[h] + int64_t(b) * cap * D;
-  const uint16_t* kc = static_cast<const uint16_t*>(a.kcache) + hb;
-  const uint16_t* vc = static_cast<const uint16_t*>(a.vcache) + hb;
-  const int32_t* lenb = a.lenb + h * a.K;
-  const int Lc = lenb[a.step];
-  const int Ltot = Lc + n;
-
-  // Q^T fragments: lane (j, hf) holds query q0+j, dims 16*kk + 8*hf + [0, 8).
-  const int qrow = qt * BM + wave * 32 + j;
-  const bool qvalid = qrow < n;
+  const int qrow = hd.qt * 128 + wave * 32 + j;
   Vec16 qf[8];
-  {
-    const uint16_t* qp = q + (int64_t(b) * n + (qvalid ? qrow : 0)) * tok + h * D + 8 * hf;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      qf[kk].u = qvalid ? *reinterpret_cast<const uint4*>(qp + 16 * kk) : make_uint4(0, 0, 0, 0);
-    }
-  }
+  load_q(hd, qrow, hf, qf);
 
-  // Staging assignment.  K: 16-byte chunk kc_c of rows kr + 16*i.
-  // V: key group vg (keys 4vg..4vg+3), 16-byte dim chunk vc_c.
-  const int k_c = tid & 15, k_r = tid >> 4;
-  const int v_g = tid & 15, v_c = tid >> 4;
-  uint4 kreg[4], vreg[4];
-
-  auto load_tile = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = k0 + k_r + 16 * i;
-      const uint16_t* p = key < Lc ? kc + int64_t(key) * D : kcur + int64_t(key - Lc) * tok;
-      kreg[i] = key < Ltot ? *reinterpret_cast<const uint4*>(p + 8 * k_c) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k0 + 4 * v_g + r;
-      const uint16_t* p = key < Lc ? vc + int64_t(key) * D : vcur + int64_t(key - Lc) * tok;
-      vreg[r] = key < Ltot ? *reinterpret_cast<const uint4*>(p + 8 * v_c) : make_uint4(0, 0, 0, 0);
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&sK[(k_r + 16 * i) * KSTR + 8 * k_c]) = kreg[i];
-    // Transpose 4 keys x 8 dims into 8 rows (dims) of 4 keys.
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint2 even, odd;
-      even.x = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-      even.y = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-      odd.x = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-      odd.y = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-      const int d = 8 * v_c + 2 * w;
-      *reinterpret_cast<uint2*>(&sV[d * VSTR + 4 * v_g]) = even;
-      *reinterpret_cast<uint2*>(&sV[(d + 1) * VSTR + 4 * v_g]) = odd;
-    }
-  };
-
-  // Running state of query j (both lane halves hold the same max; sums are per half).
+  u32x4 kreg[4], vreg[4];
   float m_run = -INFINITY;
   float l_run = 0.f;
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float sc[SCAS ? kMaxScales : 1];
+  float sc[kMaxScales];
 #pragma unroll
-  for (int s = 0; s < (SCAS ? kMaxScales : 1); ++s) sc[s] = 0.f;
-
-  // Segment bounds for S-CAS: source s < step covers [lenb[s], lenb[s+1]),
-  // the current scale covers [Lc, Ltot).
-  int seg_lo[SCAS ? kMaxScales : 1], seg_hi[SCAS ? kMaxScales : 1];
-  if constexpr (SCAS) {
-#pragma unroll
-    for (int s = 0; s < kMaxScales; ++s) {
-      seg_lo[s] = s <= a.step ? lenb[s] : 0;
-      seg_hi[s] = s < a.step ? lenb[s + 1] : (s == a.step ? Ltot : 0);
-    }
-  }
+  for (int s = 0; s < kMaxScales; ++s) sc[s] = 0.f;
 
   const int kb_row = permuted_row(j);
+  const int Ltot = hd.Ltot;
   const int ntiles = (Ltot + BN - 1) / BN;
-  load_tile(0);
+  const float c2 = a.scale_log2;
+
+  load_k(hd.ks, 0, tid, kreg);
+  load_v(hd.vs, 0, tid, vreg);
+  store_k(sK[0], tid, kreg);
+  store_v(sV[0], tid, vreg);
+  if (ntiles > 1) {
+    load_k(hd.ks, BN, tid, kreg);
+    load_v(hd.vs, BN, tid, vreg);
+  }
+  __syncthreads();
 
   for (int it = 0; it < ntiles; ++it) {
     const int k0 = it * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(k0 + BN);
+    const int buf = it & 1;
+    if (it + 1 < ntiles) {
+      store_k(sK[buf ^ 1], tid, kreg);
+      store_v(sV[buf ^ 1], tid, vreg);
+    }
+    if (it + 2 < ntiles) {
+      load_k(hd.ks, k0 + 2 * BN, tid, kreg);
+      load_v(hd.vs, k0 + 2 * BN, tid, vreg);
+    }
 
     // Scores S^T for two 32-key blocks.
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x16{};
-      const uint16_t* kp = &sK[(32 * kb + kb_row) * KSTR + 8 * hf];
+      const uint16_t* kp = &sK[buf][(32 * kb + kb_row) * KSTR + 8 * hf];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         Vec16 kf;
-        kf.u = *reinterpret_cast<const uint4*>(kp + 16 * kk);
+        kf.u = *reinterpret_cast<const u32x4*>(kp + 16 * kk);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.b, qf[kk].b, s[kb], 0, 0, 0);
       }
     }
 
-    // Register v = 4k'+r of block kb holds key 32kb + 16(k'>>1) + 8hf + 4(k'&1) + r.
     if (k0 + BN > Ltot) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kp = v >> 2, r = v & 3;
-          const int key = k0 + 32 * kb + 16 * (kp >> 1) + 8 * hf + 4 * (kp & 1) + r;
-          if (key >= Ltot) s[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (k0 + 32 * kb + key_of(v, hf) >= Ltot) s[kb][v] = -INFINITY;
     }
 
     float tmax = -INFINITY;
@@ -215,113 +378,280 @@ __global__ __launch_bounds__(kThreads, 2) void attend_bf16_d128_kernel(AttendArg
 #pragma unroll
       for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[kb][v]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax * a.scale_log2);
-    const float corr = exp2f(m_run - m_new);
-    m_run = m_new;
+    const float mt = tmax * c2;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= corr;
+      if constexpr (SCAS) {
+#pragma unroll
+        for (int src = 0; src < kMaxScales; ++src) sc[src] *= corr;
+      }
+    }
 
-    float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(fmaf(s[kb][v], a.scale_log2, -m_new));
-        s[kb][v] = p;
-        psum += p;
-      }
-    l_run = fmaf(l_run, corr, psum);
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= corr;
-
-    if constexpr (SCAS) {
-#pragma unroll
-      for (int src = 0; src < kMaxScales; ++src) {
-        sc[src] *= corr;
-        const int lo = seg_lo[src], hi = seg_hi[src];
-        if (src <= a.step && lo < hi && lo < k0 + BN && hi > k0) {
-          float acc = 0.f;
-          if (lo <= k0 && hi >= k0 + BN) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc += s[kb][v];
-          } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) {
-                const int kp = v >> 2, r = v & 3;
-                const int key = k0 + 32 * kb + 16 * (kp >> 1) + 8 * hf + 4 * (kp & 1) + r;
-                acc += (key >= lo && key < hi) ? s[kb][v] : 0.f;
-              }
-          }
-          sc[src] += acc;
-        }
-      }
-    }
+      for (int v = 0; v < 16; ++v) s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], c2, -m_run));
 
     // Probabilities as the B operand of O^T += V^T P^T, 16 keys per step.
+    Vec16 pb[4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kb = st >> 1, base = 8 * (st & 1);
-      Vec16 pb;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) pb.w[w] = pack_bf16x2(s[kb][base + 2 * w], s[kb][base + 2 * w + 1]);
+      for (int w = 0; w < 4; ++w) pb[st].w[w] = pack_bf16x2(s[kb][base + 2 * w], s[kb][base + 2 * w + 1]);
+    }
+    if constexpr (SCAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float psum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) psum += s[kb][v];
+        l_run += psum;
+        scas_add(a, hd, hf, s[kb], psum, k0 + 32 * kb, sc);
+      }
+    } else {
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        l0 = add_bf16x2(pb[st].w[0], l0);
+        l1 = add_bf16x2(pb[st].w[1], l1);
+        l0 = add_bf16x2(pb[st].w[2], l0);
+        l1 = add_bf16x2(pb[st].w[3], l1);
+      }
+      l_run += l0 + l1;
+    }
+
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         Vec16 vf;
-        vf.u = *reinterpret_cast<const uint4*>(&sV[(32 * db + j) * VSTR + 16 * st + 8 * hf]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, pb.b, oacc[db], 0, 0, 0);
+        vf.u = *reinterpret_cast<const u32x4*>(&sV[buf][(32 * db + j) * VSTR + 16 * st + 8 * hf]);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, pb[st].b, oacc[db], 0, 0, 0);
       }
-    }
-  }
-
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = 1.f / l_tot;
-
-  if (qvalid) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + (int64_t(b) * n + qrow) * tok + h * D;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int kp = 0; kp < 4; ++kp) {
-        const int d = 32 * db + 8 * kp + 4 * hf;
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][4 * kp + 0] * inv, oacc[db][4 * kp + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][4 * kp + 2] * inv, oacc[db][4 * kp + 3] * inv);
-        *reinterpret_cast<uint2*>(op + d) = w;
-      }
-  }
-
-  if constexpr (SCAS) {
-    // Mass of query j on each source, summed over this workgroup's valid queries.
-#pragma unroll
-    for (int src = 0; src < kMaxScales; ++src) {
-      float m = (sc[src] + __shfl_xor(sc[src], 32)) * inv;
-      m = qvalid ? m : 0.f;
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) m += __shfl_xor(m, off);
-      if (lane == 0) sRed[wave * kMaxScales + src] = m;
     }
     __syncthreads();
-    if (tid < kMaxScales) {
-      const float tot = sRed[tid] + sRed[kMaxScales + tid] + sRed[2 * kMaxScales + tid] +
-                        sRed[3 * kMaxScales + tid];
-      const int64_t row = (int64_t(b) * a.H + h) * a.n_qtiles + qt;
-      a.partials[row * kMaxScales + tid] = tot;
-    }
   }
+
+  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
+  store_out(a, hd, qrow, hf, oacc, inv);
+  if constexpr (SCAS) scas_reduce<4>(a, hd, qrow, inv, sc, sRed);
+}
+
+// ---------------------------------------------------------------------------
+// 256 queries per workgroup of 8 waves, 32 per wave, software-pipelined.
+// ---------------------------------------------------------------------------
+template <bool SCAS>
+__global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[3][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[3][D * VSTR];
+  __shared__ float sRed[SCAS ? 8 * kMaxScales : 1];
+
+  const Head hd = setup(a);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, hf = lane >> 5;
+  const bool kstager = tid >= 256;
+  const int stid = tid & 255;
+  const int qrow = hd.qt * 256 + wave * 32 + j;
+  Vec16 qf[8];
+  load_q(hd, qrow, hf, qf);
+
+  f32x16 o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  float sc[kMaxScales];
+#pragma unroll
+  for (int s = 0; s < kMaxScales; ++s) sc[s] = 0.f;
+
+  const int kb_row = permuted_row(j);
+  const int Ltot = hd.Ltot;
+  const int ntiles = (Ltot + BN - 1) / BN;
+  const float c2 = a.scale_log2;
+
+  auto qk = [&](const uint16_t* Kt, int kb, f32x16& s) {
+    s = f32x16{};
+    const uint16_t* kp = Kt + (32 * kb + kb_row) * KSTR + 8 * hf;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      Vec16 kf;
+      kf.u = *reinterpret_cast<const u32x4*>(kp + 16 * kk);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.b, qf[kk].b, s, 0, 0, 0);
+    }
+  };
+  auto pv = [&](const uint16_t* Vt, int kb, const Vec16 (&p)[2]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int st = 2 * kb + half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        Vec16 vf;
+        vf.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * st + 8 * hf]);
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, p[half].b, o[db], 0, 0, 0);
+      }
+    }
+  };
+  // Softmax front: tail mask (last tile only), block max, lazy rescale.  A
+  // rescale also scales the probabilities of the previous unit, whose value
+  // product is still to be issued, and the S-CAS sums, which already hold it.
+  auto front = [&](f32x16& s, int kblk, Vec16 (&pprev)[2], auto last_c) {
+    if constexpr (decltype(last_c)::value) {
+      if (kblk + 32 > Ltot) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (kblk + key_of(v, hf) >= Ltot) s[v] = -INFINITY;
+      }
+    }
+    float t = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t = fmaxf(t, s[v]);
+    t = fmaxf(t, __shfl_xor(t, 32));
+    const float mt = t * c2;
+    if (__any(mt > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= corr;
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x = pprev[half].w[w];
+          pprev[half].w[w] = pack_bf16x2(bf16_lo(x) * corr, bf16_hi(x) * corr);
+        }
+      if constexpr (SCAS) {
+#pragma unroll
+        for (int src = 0; src < kMaxScales; ++src) sc[src] *= corr;
+      }
+    }
+  };
+  // Softmax back: exponentials, bf16 packing, denominator.
+  auto back = [&](f32x16& s, Vec16 (&p)[2]) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -m_run));
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) p[half].w[w] = pack_bf16x2(s[8 * half + 2 * w], s[8 * half + 2 * w + 1]);
+    float psum = 0.f;
+    if constexpr (SCAS) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) psum += s[v];
+    } else {
+      float l1 = 0.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        psum = add_bf16x2(p[half].w[0], psum);
+        l1 = add_bf16x2(p[half].w[1], l1);
+        psum = add_bf16x2(p[half].w[2], psum);
+        l1 = add_bf16x2(p[half].w[3], l1);
+      }
+      psum += l1;
+    }
+    l_run += psum;
+    return psum;
+  };
+
+  u32x4 reg[4];  // K(t+2) on waves 4-7, V(t+1) on waves 0-3
+  f32x16 s0, s1;
+  Vec16 p0[2], p1[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) p1[half].u = u32x4{0, 0, 0, 0};
+
+  // Prologue: K(0) in buffer 0; K(1) (waves 4-7) and V(0) (waves 0-3) in registers.
+  if (kstager) {
+    load_k(hd.ks, 0, stid, reg);
+    store_k(sK[0], stid, reg);
+    if (ntiles > 1) load_k(hd.ks, BN, stid, reg);
+  } else {
+    load_v(hd.vs, 0, stid, reg);
+  }
+  __syncthreads();
+  qk(sK[0], 0, s0);
+
+  // One 64-key tile; FIRST drops the value product of the absent previous
+  // unit, LAST the score product of the absent next tile and enables the
+  // tail mask.
+  int bk = 0;  // LDS buffer of K(t) and of V(t)
+  auto tile = [&](int t, auto first_c, auto last_c) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
+    const int k0 = t * BN;
+    const int bn = bk == 2 ? 0 : bk + 1;
+    const int bp = bk == 0 ? 2 : bk - 1;
+    if (kstager) {
+      if constexpr (!LAST) store_k(sK[bn], stid, reg);
+      if (t + 2 < ntiles) load_k(hd.ks, k0 + 2 * BN, stid, reg);
+    } else {
+      store_v(sV[bk], stid, reg);
+      if constexpr (!LAST) load_v(hd.vs, k0 + BN, stid, reg);
+    }
+
+    // step a: unit (t, keys 0..31)
+    front(s0, k0, p1, last_c);
+    if constexpr (!FIRST) pv(sV[bp], 1, p1);
+    qk(sK[bk], 1, s1);
+    const float e0 = back(s0, p0);
+    if constexpr (SCAS) scas_add(a, hd, hf, s0, e0, k0, sc);
+    __syncthreads();
+
+    // step b: unit (t, keys 32..63)
+    front(s1, k0 + 32, p0, last_c);
+    pv(sV[bk], 0, p0);
+    if constexpr (!LAST) qk(sK[bn], 0, s0);
+    const float e1 = back(s1, p1);
+    if constexpr (SCAS) scas_add(a, hd, hf, s1, e1, k0 + 32, sc);
+    bk = bn;
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  if (ntiles == 1) {
+    tile(0, T_{}, T_{});
+  } else {
+    tile(0, T_{}, F_{});
+    for (int t = 1; t + 1 < ntiles; ++t) tile(t, F_{}, F_{});
+    tile(ntiles - 1, F_{}, T_{});
+  }
+  pv(sV[bk == 0 ? 2 : bk - 1], 1, p1);
+
+  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
+  store_out(a, hd, qrow, hf, o, inv);
+  if constexpr (SCAS) scas_reduce<8>(a, hd, qrow, inv, sc, sRed);
 }
 
 }  // namespace
 
+// 256-query workgroups (one per CU) when they fill at least one full round of
+// the 256 CUs; otherwise 128-query workgroups (two per CU), which spread a
+// small launch over more CUs.
+int attend_bf16_rows_per_workgroup(int B, int H, int n) {
+  const int64_t wg256 = int64_t(B) * H * ((n + 255) / 256);
+  return wg256 >= 256 ? 256 : 128;
+}
+
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
+  const int rows = attend_bf16_rows_per_workgroup(a.B, a.H, a.n);
   const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles;
-  if (scas)
-    hipLaunchKernelGGL(attend_bf16_d128_kernel<true>, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL(attend_bf16_d128_kernel<false>, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                       s, a);
+  if (a.n_qtiles != (a.n + rows - 1) / rows) return hipErrorInvalidValue;
+  if (rows == 256) {
+    if (scas)
+      hipLaunchKernelGGL(attend_q256_kernel<true>, dim3(unsigned(blocks)), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(attend_q256_kernel<false>, dim3(unsigned(blocks)), dim3(512), 0, s, a);
+  } else {
+    if (scas)
+      hipLaunchKernelGGL(attend_q128_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attend_q128_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

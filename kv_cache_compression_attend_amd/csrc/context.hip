@@ -72,7 +72,9 @@ void free_tables(hk_ctx* c) {
 }
 
 // Query rows per attend workgroup.
-int rows_per_workgroup(int dtype) { return dtype == HK_DTYPE_BF16 ? 128 : 64; }
+int rows_per_workgroup(int dtype, int B, int H, int n) {
+  return dtype == HK_DTYPE_BF16 ? hk::attend_bf16_rows_per_workgroup(B, H, n) : 64;
+}
 
 template <typename T>
 hipError_t upload(T** dst, const std::vector<T>& src) {
@@ -125,7 +127,8 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.n = c->tokens[step];
   a.K = c->K;
   a.step = step;
-  a.n_qtiles = (a.n + rows_per_workgroup(c->dtype) - 1) / rows_per_workgroup(c->dtype);
+  const int rows = rows_per_workgroup(c->dtype, c->B, c->H, a.n);
+  a.n_qtiles = (a.n + rows - 1) / rows;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
 
@@ -227,7 +230,8 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
 
   int64_t max_partials = 1;
   for (int t = 0; t < K; ++t) {
-    const int64_t qt = (scale_tokens[t] + rows_per_workgroup(dtype) - 1) / rows_per_workgroup(dtype);
+    const int rows = rows_per_workgroup(dtype, B, H, scale_tokens[t]);
+    const int64_t qt = (scale_tokens[t] + rows - 1) / rows;
     max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
   }
 

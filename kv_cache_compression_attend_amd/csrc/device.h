@@ -60,7 +60,12 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-// Launchers (defined next to their kernels).
+// Query rows per workgroup the bf16 attend launch uses for a scale of n
+// tokens (128 or 256); the S-CAS partial rows follow the same tiling.
+int attend_bf16_rows_per_workgroup(int B, int H, int n);
+
+// Launchers (defined next to their kernels).  a.n_qtiles must follow
+// attend_bf16_rows_per_workgroup for the bf16 launch.
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
 hipError_t launch_scas_finalize(const float* partials, float* table, int layer, int H, int K,

@@ -147,6 +147,22 @@ def test_bf16_ragged_tiles_and_junctions(seed):
     run.ctx.close()
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bf16_ragged_wide_launch(seed):
+    """Enough (batch, head) pairs that the launch takes the 256-query,
+    8-wave pipelined tiling: scale sizes off the 256-query and 64-key grids,
+    junctions mid-tile, single-tile and many-tile heads, S-CAS on."""
+    wl = _custom(60 + seed, f"ragged-wide-{seed}", (1, 3, 7, 13, 23), heads=16, head_dim=128,
+                 batch=16, dtype="bf16", layers=1)
+    keep = _random_keep(wl, 200 + seed)
+    run = generate(wl, keep, [0], scas=True)
+    pairs = [(b, h) for b in (0, 5, 15) for h in range(16)]
+    _compare_outputs(run, [0], rows_per_unit=600, bh=pairs)
+    _compare_scas(run, 0, steps=(3, 4), heads=(0, 1, 7, 15))
+    check_cache(run, [0])
+    run.ctx.close()
+
+
 def test_single_scale_workload():
     wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
     keep = np.zeros((1, 2, 1), dtype=np.uint8)

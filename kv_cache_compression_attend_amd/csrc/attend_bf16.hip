@@ -187,15 +187,19 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
 struct Head {
   KeySource ks, vs;
   const char* q;      // (b, row 0, h) of the query tensor
-  int n, tokb, Lc, Ltot, h, b, qt;
+  int n, tokb, Lc, Ltot, h, b, qt, split;
   const int32_t* lenb;
 };
 
 __device__ __forceinline__ Head setup(const AttendArgs& a) {
   Head hd;
+  // Logical order: (b, h, split, q-tile), q-tile fastest, so the workgroups
+  // that read the same key range of a head are adjacent.
   const int wg = xcd_logical(blockIdx.x, gridDim.x);
   hd.qt = wg % a.n_qtiles;
-  const int bh = wg / a.n_qtiles;
+  const int rest = wg / a.n_qtiles;
+  hd.split = rest % a.n_split;
+  const int bh = rest / a.n_split;
   hd.h = bh % a.H;
   hd.b = bh / a.H;
   hd.n = a.n;
@@ -325,27 +329,33 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
-  const int ntiles = (Ltot + BN - 1) / BN;
   const float c2 = a.scale_log2;
+  // Key tiles [t_lo, t_hi) of this workgroup's split.
+  const int ntiles_all = (Ltot + BN - 1) / BN;
+  const int per_split = (ntiles_all + a.n_split - 1) / a.n_split;
+  const int t_lo = hd.split * per_split;
+  const int t_hi = min(ntiles_all, t_lo + per_split);
 
-  load_k(hd.ks, 0, tid, kreg);
-  load_v(hd.vs, 0, tid, vreg);
-  store_k(sK[0], tid, kreg);
-  store_v(sV[0], tid, vreg);
-  if (ntiles > 1) {
-    load_k(hd.ks, BN, tid, kreg);
-    load_v(hd.vs, BN, tid, vreg);
+  if (t_lo < t_hi) {
+    load_k(hd.ks, t_lo * BN, tid, kreg);
+    load_v(hd.vs, t_lo * BN, tid, vreg);
+    store_k(sK[0], tid, kreg);
+    store_v(sV[0], tid, vreg);
+    if (t_lo + 1 < t_hi) {
+      load_k(hd.ks, (t_lo + 1) * BN, tid, kreg);
+      load_v(hd.vs, (t_lo + 1) * BN, tid, vreg);
+    }
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  for (int it = t_lo; it < t_hi; ++it) {
     const int k0 = it * BN;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) {
+    const int buf = (it - t_lo) & 1;
+    if (it + 1 < t_hi) {
       store_k(sK[buf ^ 1], tid, kreg);
       store_v(sV[buf ^ 1], tid, vreg);
     }
-    if (it + 2 < ntiles) {
+    if (it + 2 < t_hi) {
       load_k(hd.ks, k0 + 2 * BN, tid, kreg);
       load_v(hd.vs, k0 + 2 * BN, tid, vreg);
     }
@@ -438,9 +448,54 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     __syncthreads();
   }
 
-  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (a.n_split > 1) {
+    // Unnormalised output and (max, denominator) of this split, merged later.
+    if (qrow < hd.n) {
+      const int64_t row = (int64_t(hd.split) * a.B + hd.b) * hd.n * a.H + int64_t(qrow) * a.H + hd.h;
+      float* op = a.ws_o + row * D;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp)
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * kp + 4 * hf) =
+              make_float4(oacc[db][4 * kp], oacc[db][4 * kp + 1], oacc[db][4 * kp + 2], oacc[db][4 * kp + 3]);
+      if (hf == 0) a.ws_ml[row] = make_float2(m_run, l_tot);
+    }
+    return;
+  }
+  const float inv = 1.f / l_tot;
   store_out(a, hd, qrow, hf, oacc, inv);
   if constexpr (SCAS) scas_reduce<4>(a, hd, qrow, inv, sc, sRed);
+}
+
+// Merges the splits of one output row: with M the largest split max and
+// w_s = 2^(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s, added in split
+// order.  32 lanes per row, 4 dims per lane.
+__global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, const float2* ws_ml,
+                                                             uint16_t* out, int64_t rows, int n_split) {
+  const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  if (row >= rows) return;
+  const int d0 = 4 * (threadIdx.x & 31);
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ws_ml[sp * rows + row].x);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < n_split; ++sp) {
+    const float2 ml = ws_ml[sp * rows + row];
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    const float4 o = *reinterpret_cast<const float4*>(ws_o + (sp * rows + row) * D + d0);
+    L = fmaf(w, ml.y, L);
+    acc.x = fmaf(w, o.x, acc.x);
+    acc.y = fmaf(w, o.y, acc.y);
+    acc.z = fmaf(w, o.z, acc.z);
+    acc.w = fmaf(w, o.w, acc.w);
+  }
+  const float inv = 1.f / L;
+  uint2 wv;
+  wv.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+  wv.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(out + row * D + d0) = wv;
 }
 
 // ---------------------------------------------------------------------------
@@ -637,10 +692,41 @@ int attend_bf16_rows_per_workgroup(int B, int H, int n) {
   return wg256 >= 256 ? 256 : 128;
 }
 
+int attend_bf16_splits(int B, int H, int n, int max_keys) {
+  if (attend_bf16_rows_per_workgroup(B, H, n) != 128) return 1;
+  const int64_t wg = int64_t(B) * H * ((n + 127) / 128);
+  const int tiles = (max_keys + BN - 1) / BN;
+  // Rounds of 512 workgroup slots (two per CU) per unit of work, plus a small
+  // per-split cost for the merge.
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= 16; ++sp) {
+    if (sp > 1 && tiles < 4 * sp) break;
+    const double rounds = double((wg * sp + 511) / 512);
+    const double cost = rounds / sp + 0.03 * (sp - 1);
+    if (cost < best_cost - 1e-9) {
+      best_cost = cost;
+      best = sp;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
   const int rows = attend_bf16_rows_per_workgroup(a.B, a.H, a.n);
-  const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles;
+  const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
   if (a.n_qtiles != (a.n + rows - 1) / rows) return hipErrorInvalidValue;
+  if (a.n_split < 1 || (a.n_split > 1 && (scas || rows != 128 || !a.ws_o || !a.ws_ml)))
+    return hipErrorInvalidValue;
+  if (a.n_split > 1) {
+    hipLaunchKernelGGL(attend_q128_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t out_rows = int64_t(a.B) * a.n * a.H;
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(unsigned((out_rows + 7) / 8)), dim3(256), 0, s,
+                       a.ws_o, a.ws_ml, static_cast<uint16_t*>(a.out), out_rows, a.n_split);
+    return hipGetLastError();
+  }
   if (rows == 256) {
     if (scas)
       hipLaunchKernelGGL(attend_q256_kernel<true>, dim3(unsigned(blocks)), dim3(512), 0, s, a);

@@ -31,6 +31,9 @@ struct hk_ctx {
   int32_t* d_lenb = nullptr;
   hk::CopyDesc* d_desc = nullptr;
   float* d_partials = nullptr;
+  std::vector<int> splits;        // [K] key-range splits of each scale's attend launch
+  float* d_ws_o = nullptr;        // split workspace: unnormalised outputs
+  float2* d_ws_ml = nullptr;      // split workspace: (max, denominator)
   std::vector<int> appended;      // last scale appended per layer (-1: none)
 };
 
@@ -64,6 +67,10 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_lenb);
   (void)hipFree(c->d_desc);
   (void)hipFree(c->d_partials);
+  (void)hipFree(c->d_ws_o);
+  (void)hipFree(c->d_ws_ml);
+  c->d_ws_o = nullptr;
+  c->d_ws_ml = nullptr;
   c->d_base = nullptr;
   c->d_cap = nullptr;
   c->d_lenb = nullptr;
@@ -122,6 +129,9 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.cap = c->d_cap + int64_t(layer) * c->H;
   a.lenb = c->d_lenb + int64_t(layer) * c->H * c->K;
   a.partials = c->d_partials;
+  a.ws_o = c->d_ws_o;
+  a.ws_ml = c->d_ws_ml;
+  a.n_split = scas ? 1 : c->splits[step];
   a.B = c->B;
   a.H = c->H;
   a.n = c->tokens[step];
@@ -235,6 +245,21 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
     max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
   }
 
+  // Key-range splits per scale (bf16 launches without S-CAS that would not
+  // fill the chip) and the workspace the largest split launch needs.
+  c->splits.assign(K, 1);
+  int64_t ws_rows = 0;
+  if (dtype == HK_DTYPE_BF16) {
+    for (int t = 0; t < K; ++t) {
+      int max_keys = 0;
+      for (int64_t f = 0; f < heads; ++f)
+        max_keys = std::max<int>(max_keys, c->lenb[f * K + t] + scale_tokens[t]);
+      c->splits[t] = hk::attend_bf16_splits(B, H, scale_tokens[t], max_keys);
+      if (c->splits[t] > 1)
+        ws_rows = std::max<int64_t>(ws_rows, int64_t(c->splits[t]) * B * scale_tokens[t] * H);
+    }
+  }
+
   hipError_t e = hipGetDevice(&c->device);
   if (e == hipSuccess) e = upload(&c->d_base, c->base);
   std::vector<int32_t> cap32(c->cap.begin(), c->cap.end());
@@ -244,6 +269,10 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
   if (e == hipSuccess)
     e = hipMalloc(reinterpret_cast<void**>(&c->d_partials),
                   size_t(max_partials) * hk::kMaxScales * sizeof(float));
+  if (e == hipSuccess && ws_rows > 0)
+    e = hipMalloc(reinterpret_cast<void**>(&c->d_ws_o), size_t(ws_rows) * D * sizeof(float));
+  if (e == hipSuccess && ws_rows > 0)
+    e = hipMalloc(reinterpret_cast<void**>(&c->d_ws_ml), size_t(ws_rows) * sizeof(float2));
   if (e != hipSuccess) {
     free_tables(c);
     delete c;

@@ -22,7 +22,10 @@ struct AttendArgs {
   const int32_t* cap;     // [H] cache rows per batch entry of head (layer, h)
   const int32_t* lenb;    // [H][K] rows cached before each scale
   float* partials;        // S-CAS partial sums [B*H*n_qtiles][kMaxScales]
+  float* ws_o;            // split launches: unnormalised outputs [n_split][B][n][H][D] fp32
+  float2* ws_ml;          // split launches: (running max, denominator) [n_split][B][n][H]
   int B, H, n, K, step, n_qtiles;
+  int n_split;            // key-range splits per query tile (1: no split)
   float scale;            // softmax scale alpha
   float scale_log2;       // alpha * log2(e)
 };
@@ -64,8 +67,14 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
 // tokens (128 or 256); the S-CAS partial rows follow the same tiling.
 int attend_bf16_rows_per_workgroup(int B, int H, int n);
 
+// Key-range splits for a bf16 attend launch without S-CAS: 1 when the
+// launch fills the chip, else enough splits to give the 256 CUs two
+// workgroups each, keeping at least 4 key tiles per split of the longest head.
+int attend_bf16_splits(int B, int H, int n, int max_keys);
+
 // Launchers (defined next to their kernels).  a.n_qtiles must follow
-// attend_bf16_rows_per_workgroup for the bf16 launch.
+// attend_bf16_rows_per_workgroup and a.n_split attend_bf16_splits (or 1)
+// for the bf16 launch; a split launch also merges the splits into a.out.
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
 hipError_t launch_scas_finalize(const float* partials, float* table, int layer, int H, int K,

@@ -174,6 +174,17 @@ int hk_attend_with_scas(hk_ctx* ctx, int layer, int step, const void* q, const v
 int hk_append_scale(hk_ctx* ctx, int layer_begin, int layer_end, int step, const void* k_cur,
                     const void* v_cur, int64_t layer_stride_elems, void* hip_stream);
 
+/* The launch plan hk_attend / hk_attend_with_scas use for scale `step`:
+ * query rows per workgroup (bf16: 128 or 256, fp32: 64) and key-range splits
+ * (1 = none; an S-CAS launch never splits).  A split launch is followed by a
+ * merge kernel.  For tools and benchmarks that attribute kernel time.
+ *   with_scas           0 for hk_attend, 1 for hk_attend_with_scas
+ *   rows_per_workgroup  host int32 (written)
+ *   splits              host int32 (written)
+ * Errors: HK_EINVAL. */
+int hk_attend_plan(const hk_ctx* ctx, int step, int with_scas, int32_t* rows_per_workgroup,
+                   int32_t* splits);
+
 /* Token slots per sequence held by the whole cache (all layers and heads)
  * once scale `step` has been appended: sum over kept s <= min(step, K-2). */
 int hk_retained_tokens(const hk_ctx* ctx, int step, int64_t* out);

@@ -53,7 +53,7 @@ def library_path() -> str:
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m kv_cache_compression_attend_amd.build` "
+            f"{_LIB_PATH} is not built; run `python kv_cache_compression_attend_amd/build.py` "
             "(there is no CPU fallback)")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, I64, D, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float
@@ -68,6 +68,7 @@ def _load():
         "hk_attend_with_scas": ([P, I, I, P, P, P, P, F, P, P], I),
         "hk_append_scale": ([P, I, I, I, P, P, I64, P], I),
         "hk_retained_tokens": ([P, I, P], I),
+        "hk_attend_plan": ([P, I, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -232,6 +233,13 @@ class Context:
             stride = int(np.prod(per))
         _check(_lib.hk_append_scale(self._handle(), int(layer_begin), int(layer_end), int(step),
                                     ptrs[0], ptrs[1], stride if nl > 1 else 0, _stream(stream)))
+
+    def attend_plan(self, step: int, with_scas: bool = False) -> Tuple[int, int]:
+        """(query rows per workgroup, key-range splits) of scale ``step``'s launch."""
+        rows, splits = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.hk_attend_plan(self._handle(), int(step), int(bool(with_scas)),
+                                   ctypes.byref(rows), ctypes.byref(splits)))
+        return rows.value, splits.value
 
     def retained_tokens(self, step: int) -> int:
         out = ctypes.c_int64()

@@ -1,7 +1,8 @@
 """Build libheatkv.so in-tree: host C++ with g++, HIP kernels with hipcc for gfx950.
 
-Usage: python -m kv_cache_compression_attend_amd.build  (or call build()).
-Always recompiles every source.
+Usage: python kv_cache_compression_attend_amd/build.py  (run by path: importing
+the package would load the library being rebuilt).  Always recompiles every
+source.
 """
 from __future__ import annotations
 

@@ -368,3 +368,12 @@ extern "C" int hk_retained_tokens(const hk_ctx* c, int step, int64_t* out) {
   *out = c->retained[step];
   return HK_OK;
 }
+
+extern "C" int hk_attend_plan(const hk_ctx* c, int step, int with_scas, int32_t* rows_per_wg,
+                              int32_t* splits) {
+  if (!c || !rows_per_wg || !splits) return fail(HK_EINVAL, "null argument");
+  if (step < 0 || step >= c->K) return fail(HK_EINVAL, "step %d out of [0, %d)", step, c->K);
+  *rows_per_wg = rows_per_workgroup(c->dtype, c->B, c->H, c->tokens[step]);
+  *splits = with_scas ? 1 : c->splits[step];
+  return HK_OK;
+}

@@ -15,8 +15,10 @@ HEADER = os.path.join(ROOT, "include", "heatkv.h")
 LIB = os.path.join(ROOT, "kv_cache_compression_attend_amd", "libheatkv.so")
 
 if not os.path.exists(LIB):  # build only when nothing is built
-    from kv_cache_compression_attend_amd import build as _build
-    _build.build()
+    import subprocess
+    import sys
+    subprocess.run([sys.executable, os.path.join(ROOT, "kv_cache_compression_attend_amd", "build.py")],
+                   check=True)
 
 import kv_cache_compression_attend_amd as hk  # noqa: E402
 
@@ -29,7 +31,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -114,6 +116,8 @@ def test_null_and_range_errors_without_gpu():
     assert lib.hk_attend(None, 0, 0, None, None, None, None, 1.0, None) == hk.HK_EINVAL
     assert lib.hk_append_scale(None, 0, 1, 0, None, None, 0, None) == hk.HK_EINVAL
     assert lib.hk_reset(None) == hk.HK_EINVAL
+    r32 = ctypes.c_int32()
+    assert lib.hk_attend_plan(None, 0, 0, ctypes.byref(r32), ctypes.byref(r32)) == hk.HK_EINVAL
     assert lib.hk_destroy(None) == hk.HK_OK
     out = ctypes.c_int64()
     assert lib.hk_retained_tokens(None, 0, ctypes.byref(out)) == hk.HK_EINVAL

@@ -3,9 +3,10 @@
 
 A step is one generation pass of the whole hot path over one batch: for every
 scale t = 0..K-1 and every layer, block-causal attention over the kept cache
-segments plus the current scale (hk_attend), and after every scale but the
-last, one compaction of all layers' kept segments into the ragged cache
-(hk_append_scale).  Inputs are synthetic and already resident in HBM when the
+segments plus the current scale, with the scale's kept segments compacted into
+the ragged cache in the same launch (hk_attend_append; the final scale is only
+attended).  The same pass with separate hk_attend / hk_append_scale calls is
+timed beside it.  Inputs are synthetic and already resident in HBM when the
 timed region starts.
 
 Default workload: one Infinity-2B-shaped layer at full cache (16 heads,
@@ -13,9 +14,10 @@ head_dim 128, batch 1, 13 scales with sides 1..64, 10,521 tokens), bf16.
 ``value`` is attention TFLOP/s over the whole pass (algorithmic flops
 4*d*n_q*n_k summed over all attention launches, divided by the pass time).
 
-Also reported: the attention kernel's roofline (MFMA bf16), compaction GB/s,
-the 32-layer batch-8 10%-budget workload's scales/s per image, and the fp64
-CPU oracle timed on a bounded sample on this host.
+Also reported: the 256-query attention kernel's roofline (MFMA bf16), the
+32-layer batch-8 10%-budget workload's scales/s per image, standalone
+compaction GB/s (HBM roofline) on the 32-layer batch-4 full-cache workload,
+and the fp64 CPU oracle timed on the same full-cache pass on this host.
 """
 from __future__ import annotations
 
@@ -139,24 +141,30 @@ def main():
     total_flops = sum(flops.values())
 
     def one_pass(rec=None):
+        """One generation pass: attention of every (layer, scale) with the
+        scale's compaction fused into the same launch."""
         ctx.reset()
         for t in range(K):
             for l in range(L):
                 if rec is not None:
                     rec[("a", l, t)][0].record(stream)
-                ctx.attend(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
-                           stream=stream)
+                ctx.attend_append(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                                  stream=stream)
                 if rec is not None:
                     rec[("a", l, t)][1].record(stream)
+
+    def unfused_pass():
+        """The same pass with attention and compaction as separate calls."""
+        ctx.reset()
+        for t in range(K):
+            for l in range(L):
+                ctx.attend(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                           stream=stream)
             if t < K - 1:
-                if rec is not None:
-                    rec[("c", t)][0].record(stream)
                 if L == 1:
                     ctx.append_scale(0, 1, t, kall[t][0], vall[t][0], stream=stream)
                 else:
                     ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
-                if rec is not None:
-                    rec[("c", t)][1].record(stream)
 
     for _ in range(args.warmup):
         one_pass()
@@ -179,15 +187,21 @@ def main():
         for t in range(K):
             for l in range(L):
                 rec[("a", l, t)] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            if t < K - 1:
-                rec[("c", t)] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         one_pass(rec)
         recs.append(rec)
     torch.cuda.synchronize()
     attend_ms = {key: np.mean([r[key][0].elapsed_time(r[key][1]) for r in recs])
                  for key in recs[0] if key[0] == "a"}
-    compact_ms = {key: np.mean([r[key][0].elapsed_time(r[key][1]) for r in recs])
-                  for key in recs[0] if key[0] == "c"}
+
+    for _ in range(2):
+        unfused_pass()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        unfused_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_unfused = t0.elapsed_time(t1) / args.steps
     attend_total_ms = sum(attend_ms.values())
     attend_tflops = total_flops / (attend_total_ms * 1e-3) / 1e12
     n_launch = len(attend_ms)
@@ -197,10 +211,6 @@ def main():
     q256_flops = sum(flops[(k[1], k[2])] for k in q256)
     q256_tflops = q256_flops / (q256_ms * 1e-3) / 1e12 if q256 else 0.0
     per_step = {t: round(flops[(0, t)] / (attend_ms[("a", 0, t)] * 1e-3) / 1e12, 1) for t in range(K)}
-    cbytes = {t: compact_bytes(wl, keep, t, slice(0, L)) for t in range(K - 1)}
-    compact_gbps = sum(cbytes.values()) / (sum(compact_ms.values()) * 1e-3) / 1e9
-    c_big = max(cbytes, key=lambda t: cbytes[t])
-    compact_big_gbps = cbytes[c_big] / (compact_ms[("c", c_big)] * 1e-3) / 1e9
 
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -225,7 +235,7 @@ def main():
         "data": "synthetic (seeded N(0,1) draws rounded to bf16; no model weights)",
         "config": {"workload": "infinity2b-layer-full-b1: 1 layer x 16 heads x head_dim 128, "
                                "batch 1, 13 scales (sides 1..64, 10,521 tokens), 100% budget; "
-                               "13 attention launches + 12 compactions per step",
+                               "13 attend_append calls per step (compaction fused)",
                    "global_batch": wl.batch, "seq_len": wl.total_tokens,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": ROOFLINE_KERNEL,
@@ -241,8 +251,8 @@ def main():
                                 "avg_launch_us": round(attend_total_ms / n_launch * 1e3, 2)},
         "attend_plan_per_step": {t: list(ctx.attend_plan(t)) for t in range(K)},
         "attend_tflops_per_step": per_step,
-        "compact": {"GBps": round(compact_gbps, 1), "frac_hbm": round(compact_gbps / PEAK_HBM_GBPS, 4),
-                    "largest_step": c_big, "largest_step_GBps": round(compact_big_gbps, 1)},
+        "unfused_ms_per_step": round(ms_unfused, 4),
+        "unfused_value": round(total_flops / (ms_unfused * 1e-3) / 1e12, 2),
     }
     ctx.close()
     del qs, kall, vall, outs
@@ -251,6 +261,7 @@ def main():
     # ---------------- 32 layers, batch 8, 10% budget: scales/s per image ----------------
     if not args.no_pruned:
         result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
+        result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
 
     # ---------------- fp64 CPU oracle on a bounded sample ----------------
     if not args.no_cpu_baseline:
@@ -281,10 +292,8 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
         ctx.reset()
         for t in range(K):
             for l in range(L):
-                ctx.attend(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
-                           stream=stream)
-            if t < K - 1:
-                ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+                ctx.attend_append(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                                  stream=stream)
 
     one_pass()
     torch.cuda.synchronize()
@@ -305,6 +314,46 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
             "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
             "passes": args.pruned_steps,
             "inputs": "torch.randn on the GPU (seeded), same distribution as the parity inputs"}
+
+
+def compact_rate(args, hk, workloads, torch, np, dev, stream):
+    """Standalone compaction (hk_append_scale over all 32 layers per completed
+    scale) of the batch-4 full-cache workload: 13.5 GB moved per pass."""
+    wl = workloads.get("c3")
+    keep = workloads.full_keep(wl)
+    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
+                     torch.bfloat16)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    K, L = wl.n_scales, wl.layers
+    kall, vall = [], []
+    for t in range(K - 1):
+        shape = (L, wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim)
+        kall.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        vall.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+    nbytes = {t: compact_bytes(wl, keep, t, slice(0, L)) for t in range(K - 1)}
+    ev = {t: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for t in range(K - 1)}
+    times = {t: [] for t in range(K - 1)}
+    for rep in range(4):
+        ctx.reset()
+        for t in range(K - 1):
+            ev[t][0].record(stream)
+            ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+            ev[t][1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            for t in range(K - 1):
+                times[t].append(ev[t][0].elapsed_time(ev[t][1]))
+    ms = {t: float(np.mean(times[t])) for t in times}
+    big = max(nbytes, key=lambda t: nbytes[t])
+    total = sum(nbytes.values()) / (sum(ms.values()) * 1e-3) / 1e9
+    bigr = nbytes[big] / (ms[big] * 1e-3) / 1e9
+    ctx.close()
+    return {"workload": "infinity2b-l32-b4 full cache: one all-layer append per completed scale",
+            "bound": "hbm", "GBps": round(total, 1), "frac_hbm": round(total / PEAK_HBM_GBPS, 4),
+            "largest_step": big, "largest_step_bytes": nbytes[big],
+            "largest_step_GBps": round(bigr, 1), "largest_step_frac_hbm": round(bigr / PEAK_HBM_GBPS, 4),
+            "per_step_GBps": {t: round(nbytes[t] / (ms[t] * 1e-3) / 1e9, 1) for t in ms}}
 
 
 def cpu_baseline(args, wl, keep):

@@ -158,6 +158,19 @@ int hk_attend_with_scas(hk_ctx* ctx, int layer, int step, const void* q, const v
                         const void* v_cur, void* out, float softmax_scale,
                         float* scas_table, void* hip_stream);
 
+/* hk_attend (or, with scas_table != NULL, hk_attend_with_scas) of scale
+ * `step` in `layer`, followed by hk_append_scale of the same scale and layer,
+ * for callers that run the two back to back.  With bf16 both happen in one
+ * launch: the workgroups of query tile 0, which stage every key and value of
+ * the current scale anyway, also write the kept rows into the cache (rows
+ * the launch itself never reads), so the scale is read from HBM once instead
+ * of twice.  The final scale (step = K-1) is only attended.
+ * Order: as hk_attend, and the layer's last appended scale must be step-1.
+ * Errors: as hk_attend. */
+int hk_attend_append(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,
+                     const void* v_cur, void* out, float softmax_scale, float* scas_table,
+                     void* hip_stream);
+
 /* Compact scale `step` into the cache for layers [layer_begin, layer_end):
  * for every kept (l, h) (keep[l][h][step] = 1) and every b, copies the rows
  * k_cur_l[b][:][h][:] (and likewise V) to rows

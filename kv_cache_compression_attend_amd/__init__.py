@@ -69,6 +69,7 @@ def _load():
         "hk_append_scale": ([P, I, I, I, P, P, I64, P], I),
         "hk_retained_tokens": ([P, I, P], I),
         "hk_attend_plan": ([P, I, I, P, P], I),
+        "hk_attend_append": ([P, I, I, P, P, P, P, F, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +211,23 @@ class Context:
         _check(_lib.hk_attend_with_scas(self._handle(), int(layer), int(step), *args,
                                         float(softmax_scale), ctypes.c_void_p(scas_table.data_ptr()),
                                         _stream(stream)))
+
+    def attend_append(self, layer: int, step: int, q, k, v, out, softmax_scale: float,
+                      scas_table: Optional[torch.Tensor] = None, stream=None) -> None:
+        """attend (with S-CAS when a table is given), then append this scale of
+        this layer; one launch for bf16."""
+        if not (0 <= step < self.K):
+            raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+        args = [self._step_tensor(t, step, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+        table = None
+        if scas_table is not None:
+            want = (self.L, self.H, self.K, self.K)
+            if (tuple(scas_table.shape) != want or scas_table.dtype != torch.float32
+                    or scas_table.device != self.device or not scas_table.is_contiguous()):
+                raise HeatKVError(HK_EINVAL, f"scas_table must be a contiguous float32 {want} device tensor")
+            table = ctypes.c_void_p(scas_table.data_ptr())
+        _check(_lib.hk_attend_append(self._handle(), int(layer), int(step), *args,
+                                     float(softmax_scale), table, _stream(stream)))
 
     def append_scale(self, layer_begin: int, layer_end: int, step: int, k, v,
                      stream=None) -> None:

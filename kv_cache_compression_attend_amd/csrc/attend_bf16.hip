@@ -47,10 +47,14 @@
 //     a wave runs the score product QK(u) (8 MFMAs), the softmax SM(u) and
 //     the value product PV(u) (8 MFMAs), pipelined as step
 //     i = { PV(u_{i-1}), QK(u_{i+1}) } on the matrix cores beside SM(u_i) on
-//     the vector ALUs.  K tiles are staged one tile ahead of V tiles (waves
-//     4-7 load K, waves 0-3 load V) in three LDS buffers each, one barrier
-//     per 64 keys.  The first and last tiles are separate instantiations, so
-//     the steady-state step is straight-line code.
+//     the vector ALUs.  Each step is written as 16 fixed slots (LDS read of
+//     the fragment two slots ahead, one MFMA, one exponential and its share of
+//     the packing and sum) fenced by scheduling barriers, so LDS latency hides
+//     behind the MFMA before it and the exponentials fill the MFMA shadow.
+//     K tiles are staged one tile ahead of V tiles (waves 4-7 load K, waves
+//     0-3 load V) in three LDS buffers each, one barrier per 64 keys.  The
+//     first and last tiles are separate instantiations, so the steady-state
+//     step is straight-line code.
 #include <math.h>
 
 #include <type_traits>
@@ -183,12 +187,27 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
   }
 }
 
+// Fused append: the 16-byte chunks held in reg (rows r0 + rstep * i, chunk c
+// of the tile at key k0) whose key falls in the current scale are written to
+// the same key's row of the cache, where the scale's segment starts at row Lc.
+__device__ __forceinline__ void append_rows(const KeySource& s, char* cache, int k0, int r0, int rstep,
+                                            int c, const u32x4 (&reg)[4]) {
+  if (k0 + BN <= s.Lc) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int key = k0 + r0 + rstep * i;
+    if (key >= s.Lc && key < s.Ltot)
+      *reinterpret_cast<u32x4*>(cache + int64_t(key) * kRowBytes + 16 * c) = reg[i];
+  }
+}
+
 // Per-workgroup setup shared by both tilings.
 struct Head {
   KeySource ks, vs;
   const char* q;      // (b, row 0, h) of the query tensor
   int n, tokb, Lc, Ltot, h, b, qt, split;
   const int32_t* lenb;
+  bool append;        // this workgroup writes the current scale's rows to the cache
 };
 
 __device__ __forceinline__ Head setup(const AttendArgs& a) {
@@ -216,6 +235,9 @@ __device__ __forceinline__ Head setup(const AttendArgs& a) {
   hd.vs = KeySource{static_cast<const char*>(a.vcache) + hb, static_cast<const char*>(a.vcur) + curoff,
                     hd.Lc, hd.Ltot, hd.n, hd.tokb};
   hd.q = static_cast<const char*>(a.q) + curoff;
+  // One workgroup per (b, h, split) appends: the one with q-tile 0.  A pruned
+  // segment (no cache rows reserved for this scale) is never written.
+  hd.append = a.append && hd.qt == 0 && a.step + 1 < a.K && hd.lenb[a.step + 1] > hd.Lc;
   return hd;
 }
 
@@ -336,11 +358,21 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   const int t_lo = hd.split * per_split;
   const int t_hi = min(ntiles_all, t_lo + per_split);
 
+  char* const kc_w = const_cast<char*>(hd.ks.cache);
+  char* const vc_w = const_cast<char*>(hd.vs.cache);
+  auto append_tile = [&](int k0) {
+    if (hd.append) {
+      append_rows(hd.ks, kc_w, k0, tid >> 4, 16, tid & 15, kreg);
+      append_rows(hd.vs, vc_w, k0, 4 * (tid & 15), 1, tid >> 4, vreg);
+    }
+  };
+
   if (t_lo < t_hi) {
     load_k(hd.ks, t_lo * BN, tid, kreg);
     load_v(hd.vs, t_lo * BN, tid, vreg);
     store_k(sK[0], tid, kreg);
     store_v(sV[0], tid, vreg);
+    append_tile(t_lo * BN);
     if (t_lo + 1 < t_hi) {
       load_k(hd.ks, (t_lo + 1) * BN, tid, kreg);
       load_v(hd.vs, (t_lo + 1) * BN, tid, vreg);
@@ -354,6 +386,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     if (it + 1 < t_hi) {
       store_k(sK[buf ^ 1], tid, kreg);
       store_v(sV[buf ^ 1], tid, vreg);
+      append_tile(k0 + BN);
     }
     if (it + 2 < t_hi) {
       load_k(hd.ks, k0 + 2 * BN, tid, kreg);
@@ -588,29 +621,61 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       }
     }
   };
-  // Softmax back: exponentials, bf16 packing, denominator.
-  auto back = [&](f32x16& s, Vec16 (&p)[2]) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -m_run));
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) p[half].w[w] = pack_bf16x2(s[8 * half + 2 * w], s[8 * half + 2 * w + 1]);
-    float psum = 0.f;
-    if constexpr (SCAS) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) psum += s[v];
-    } else {
-      float l1 = 0.f;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        psum = add_bf16x2(p[half].w[0], psum);
-        l1 = add_bf16x2(p[half].w[1], l1);
-        psum = add_bf16x2(p[half].w[2], psum);
-        l1 = add_bf16x2(p[half].w[3], l1);
+  // One pipelined step in 16 fixed slots: slot i issues the LDS read of the
+  // fragment two slots ahead, one MFMA (value product of the previous unit in
+  // slots 0-7, score product of the next unit in slots 8-15) and 1/16 of the
+  // current unit's exponentials, packing and denominator.
+  auto step = [&](const uint16_t* Vt, int kbv, const Vec16 (&pprev)[2], auto do_pv_c,
+                  const uint16_t* Kt, int kbk, f32x16& snext, auto do_qk_c, f32x16& s,
+                  Vec16 (&p)[2]) {
+    constexpr bool DO_PV = decltype(do_pv_c)::value;
+    constexpr bool DO_QK = decltype(do_qk_c)::value;
+    const uint16_t* kp = Kt + (32 * kbk + kb_row) * KSTR + 8 * hf;
+    auto frag = [&](int i) {
+      Vec16 f;
+      if (i < 8) {
+        const int half = i >> 2, db = i & 3;
+        f.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * (2 * kbv + half) + 8 * hf]);
+      } else {
+        f.u = *reinterpret_cast<const u32x4*>(kp + 16 * (i - 8));
       }
-      psum += l1;
+      return f;
+    };
+    constexpr int first = DO_PV ? 0 : 8;
+    constexpr int last = DO_QK ? 16 : 8;
+    Vec16 fr[3];
+    if constexpr (first < last) fr[first % 3] = frag(first);
+    if constexpr (first + 1 < last) fr[(first + 1) % 3] = frag(first + 1);
+    if constexpr (DO_QK) snext = f32x16{};
+    float psum = 0.f, l1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i >= first && i < last) {
+        if (i + 2 < last) fr[(i + 2) % 3] = frag(i + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 8) {
+          const int half = i >> 2, db = i & 3;
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3].b, pprev[half].b, o[db], 0, 0, 0);
+        } else {
+          snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[i % 3].b, qf[i - 8].b, snext, 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_run));
+      if (i & 1) {
+        const int half = i >> 3, w = (i & 7) >> 1;
+        p[half].w[w] = pack_bf16x2(s[i - 1], s[i]);
+        if constexpr (SCAS) {
+          psum += s[i - 1];
+          l1 += s[i];
+        } else {
+          if (w & 1) l1 = add_bf16x2(p[half].w[w], l1);
+          else psum = add_bf16x2(p[half].w[w], psum);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    psum += l1;
     l_run += psum;
     return psum;
   };
@@ -622,9 +687,12 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   for (int half = 0; half < 2; ++half) p1[half].u = u32x4{0, 0, 0, 0};
 
   // Prologue: K(0) in buffer 0; K(1) (waves 4-7) and V(0) (waves 0-3) in registers.
+  char* const kc_w = const_cast<char*>(hd.ks.cache);
+  char* const vc_w = const_cast<char*>(hd.vs.cache);
   if (kstager) {
     load_k(hd.ks, 0, stid, reg);
     store_k(sK[0], stid, reg);
+    if (hd.append) append_rows(hd.ks, kc_w, 0, stid >> 4, 16, stid & 15, reg);
     if (ntiles > 1) load_k(hd.ks, BN, stid, reg);
   } else {
     load_v(hd.vs, 0, stid, reg);
@@ -643,26 +711,28 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     const int bn = bk == 2 ? 0 : bk + 1;
     const int bp = bk == 0 ? 2 : bk - 1;
     if (kstager) {
-      if constexpr (!LAST) store_k(sK[bn], stid, reg);
+      if constexpr (!LAST) {
+        store_k(sK[bn], stid, reg);
+        if (hd.append) append_rows(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
+      }
       if (t + 2 < ntiles) load_k(hd.ks, k0 + 2 * BN, stid, reg);
     } else {
       store_v(sV[bk], stid, reg);
+      if (hd.append) append_rows(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
       if constexpr (!LAST) load_v(hd.vs, k0 + BN, stid, reg);
     }
 
     // step a: unit (t, keys 0..31)
     front(s0, k0, p1, last_c);
-    if constexpr (!FIRST) pv(sV[bp], 1, p1);
-    qk(sK[bk], 1, s1);
-    const float e0 = back(s0, p0);
+    const float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
+                          std::true_type{}, s0, p0);
     if constexpr (SCAS) scas_add(a, hd, hf, s0, e0, k0, sc);
     __syncthreads();
 
     // step b: unit (t, keys 32..63)
     front(s1, k0 + 32, p0, last_c);
-    pv(sV[bk], 0, p0);
-    if constexpr (!LAST) qk(sK[bn], 0, s0);
-    const float e1 = back(s1, p1);
+    const float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
+                          std::integral_constant<bool, !LAST>{}, s1, p1);
     if constexpr (SCAS) scas_add(a, hd, hf, s1, e1, k0 + 32, sc);
     bk = bn;
   };

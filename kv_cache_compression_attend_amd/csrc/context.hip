@@ -99,9 +99,12 @@ int check_step_args(const hk_ctx* c, int layer, int step) {
   return HK_OK;
 }
 
+int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const void* k_cur,
+                  const void* v_cur, int64_t layer_stride_elems, void* hip_stream);
+
 int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
                   const void* v_cur, void* out, float softmax_scale, float* scas_table,
-                  bool scas, void* hip_stream) {
+                  bool scas, bool append, void* hip_stream) {
   int rc = check_step_args(c, layer, step);
   if (rc != HK_OK) return rc;
   if (!q || !k_cur || !v_cur || !out) return fail(HK_EINVAL, "null tensor pointer");
@@ -113,6 +116,11 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   if (step > 0 && c->appended[layer] < step - 1)
     return fail(HK_EORDER, "attend(layer %d, step %d) needs scale %d appended first (last: %d)",
                 layer, step, step - 1, c->appended[layer]);
+  // Appending this scale as well needs the layer's cache to end at scale step-1.
+  append = append && step <= c->K - 2;
+  if (append && c->appended[layer] != step - 1)
+    return fail(HK_EORDER, "append(layer %d, step %d) out of order (last appended: %d)", layer,
+                step, c->appended[layer]);
 
   DeviceGuard g(c->device);
   if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
@@ -141,6 +149,9 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.n_qtiles = (a.n + rows - 1) / rows;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  // bf16 kernels append in the same launch; the fp32 path runs the
+  // compaction kernel after the attention kernel.
+  a.append = append && c->dtype == HK_DTYPE_BF16;
 
   hipError_t e = c->dtype == HK_DTYPE_BF16 ? hk::launch_attend_bf16_d128(a, scas, s)
                                            : hk::launch_attend_f32(a, c->D, scas, s);
@@ -149,6 +160,14 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
     e = hk::launch_scas_finalize(c->d_partials, scas_table, layer, c->H, c->K, c->B, a.n, step,
                                  a.n_qtiles, s);
     if (e != hipSuccess) return hip_fail(e, "S-CAS finalize launch");
+  }
+  if (append) {
+    if (c->dtype == HK_DTYPE_BF16) {
+      c->appended[layer] = step;
+    } else {
+      rc = append_launch(c, layer, layer + 1, step, k_cur, v_cur, 0, hip_stream);
+      if (rc != HK_OK) return rc;
+    }
   }
   return HK_OK;
 }
@@ -303,15 +322,22 @@ extern "C" int hk_reset(hk_ctx* c) {
 
 extern "C" int hk_attend(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
                          const void* v_cur, void* out, float softmax_scale, void* hip_stream) {
-  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, nullptr, false,
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, nullptr, false, false,
                        hip_stream);
 }
 
 extern "C" int hk_attend_with_scas(hk_ctx* c, int layer, int step, const void* q,
                                    const void* k_cur, const void* v_cur, void* out,
                                    float softmax_scale, float* scas_table, void* hip_stream) {
-  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, scas_table, true,
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, scas_table, true, false,
                        hip_stream);
+}
+
+extern "C" int hk_attend_append(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
+                                const void* v_cur, void* out, float softmax_scale,
+                                float* scas_table, void* hip_stream) {
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, scas_table,
+                       scas_table != nullptr, true, hip_stream);
 }
 
 extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int step,
@@ -333,7 +359,17 @@ extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int st
     if (c->appended[l] != step - 1)
       return fail(HK_EORDER, "append(layer %d, step %d) out of order (last appended: %d)", l,
                   step, c->appended[l]);
+  return append_launch(c, layer_begin, layer_end, step, k_cur, v_cur, layer_stride_elems,
+                       hip_stream);
+}
 
+namespace {
+
+// Launches the compaction of scale `step` for layers [layer_begin, layer_end)
+// (arguments already checked) and records the layers as appended.
+int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const void* k_cur,
+                  const void* v_cur, int64_t layer_stride_elems, void* hip_stream) {
+  const int nl = layer_end - layer_begin;
   const int64_t first = c->desc_first[int64_t(step) * (c->L + 1) + layer_begin];
   const int64_t last = c->desc_first[int64_t(step) * (c->L + 1) + layer_end];
   if (last > first) {
@@ -361,6 +397,8 @@ extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int st
   for (int l = layer_begin; l < layer_end; ++l) c->appended[l] = step;
   return HK_OK;
 }
+
+}  // namespace
 
 extern "C" int hk_retained_tokens(const hk_ctx* c, int step, int64_t* out) {
   if (!c || !out) return fail(HK_EINVAL, "null argument");

@@ -26,6 +26,8 @@ struct AttendArgs {
   float2* ws_ml;          // split launches: (running max, denominator) [n_split][B][n][H]
   int B, H, n, K, step, n_qtiles;
   int n_split;            // key-range splits per query tile (1: no split)
+  int append;             // 1: q-tile-0 workgroups also write this scale's kept
+                          // K/V rows into the cache (fused append)
   float scale;            // softmax scale alpha
   float scale_log2;       // alpha * log2(e)
 };

@@ -62,8 +62,9 @@ class Run:
 
 
 def generate(wl, keep: np.ndarray, layers: Sequence[int], seed: int = 0, scas: bool = False,
-             multi_layer_append: bool = False, keep_inputs: bool = True) -> Run:
-    """Run all K scales for ``layers`` through the library (attend, then append)."""
+             multi_layer_append: bool = False, keep_inputs: bool = True, fused: bool = False) -> Run:
+    """Run all K scales for ``layers`` through the library: attend then append,
+    or (fused) the single attend_append call per layer and scale."""
     ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
                      torch_dtype(wl))
     poison(ctx)
@@ -80,19 +81,21 @@ def generate(wl, keep: np.ndarray, layers: Sequence[int], seed: int = 0, scas: b
                 run.inputs[l].append(inp)
             q, k, v = to_device(inp.q, wl), to_device(inp.k, wl), to_device(inp.v, wl)
             out = torch.empty_like(q)
-            note(f"{wl.name} layer {l} step {t}: {'attend_with_scas' if scas else 'attend'} "
-                 f"q {tuple(q.shape)}")
-            if scas:
+            call = "attend_append" if fused else ("attend_with_scas" if scas else "attend")
+            note(f"{wl.name} layer {l} step {t}: {call} q {tuple(q.shape)}")
+            if fused:
+                ctx.attend_append(l, t, q, k, v, out, wl.softmax_scale, table)
+            elif scas:
                 ctx.attend_with_scas(l, t, q, k, v, out, wl.softmax_scale, table)
             else:
                 ctx.attend(l, t, q, k, v, out, wl.softmax_scale)
             run.outs[(l, t)] = to_host_bits(out)
             ks.append(k)
             vs.append(v)
-            if t < wl.n_scales - 1 and not multi_layer_append:
+            if t < wl.n_scales - 1 and not multi_layer_append and not fused:
                 note(f"{wl.name} layer {l} step {t}: append_scale")
                 ctx.append_scale(l, l + 1, t, k, v)
-        if t < wl.n_scales - 1 and multi_layer_append:
+        if t < wl.n_scales - 1 and multi_layer_append and not fused:
             assert list(layers) == list(range(layers[0], layers[0] + len(layers)))
             note(f"{wl.name} layers {layers[0]}..{layers[-1]} step {t}: append_scale")
             ctx.append_scale(layers[0], layers[-1] + 1, t, torch.stack(ks), torch.stack(vs))

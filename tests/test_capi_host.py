@@ -31,7 +31,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -115,6 +115,7 @@ def test_null_and_range_errors_without_gpu():
     lib = hk._lib
     assert lib.hk_attend(None, 0, 0, None, None, None, None, 1.0, None) == hk.HK_EINVAL
     assert lib.hk_append_scale(None, 0, 1, 0, None, None, 0, None) == hk.HK_EINVAL
+    assert lib.hk_attend_append(None, 0, 0, None, None, None, None, 1.0, None, None) == hk.HK_EINVAL
     assert lib.hk_reset(None) == hk.HK_EINVAL
     r32 = ctypes.c_int32()
     assert lib.hk_attend_plan(None, 0, 0, ctypes.byref(r32), ctypes.byref(r32)) == hk.HK_EINVAL

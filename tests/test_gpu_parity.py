@@ -166,6 +166,59 @@ def test_bf16_ragged_wide_launch(seed):
     run.ctx.close()
 
 
+@pytest.mark.parametrize("case", ["full-b1", "pruned-b8", "ragged-f32", "ragged-bf16-scas", "wide-scas"])
+def test_fused_attend_append(case):
+    """attend_append (attention and this scale's append in one call) leaves the
+    same cache as attend + append_scale and the same outputs, across both bf16
+    tilings, split launches, junctions, pruned heads and the fp32 path."""
+    if case == "full-b1":
+        wl, layers, scas = workloads.get("c1"), [0], False
+        keep = _schedule(wl)
+    elif case == "pruned-b8":
+        wl, layers, scas = workloads.get("c2"), [5], False
+        keep = _schedule(wl)
+    elif case == "ragged-f32":
+        wl = _custom(70, "fused-f32", (1, 3, 5, 7, 9), heads=3, head_dim=16, batch=2, dtype="f32", layers=2)
+        keep, layers, scas = _random_keep(wl, 70), [0, 1], True
+    elif case == "ragged-bf16-scas":
+        wl = _custom(71, "fused-bf16", (1, 3, 5, 7, 11, 13, 17, 19, 23), heads=5, head_dim=128,
+                     batch=3, dtype="bf16", layers=2)
+        keep, layers, scas = _random_keep(wl, 71), [0, 1], True
+    else:
+        wl = _custom(72, "fused-wide", (1, 3, 7, 13, 23), heads=16, head_dim=128, batch=16,
+                     dtype="bf16", layers=1)
+        keep, layers, scas = _random_keep(wl, 72), [0], True
+    run = generate(wl, keep, layers, scas=scas, fused=True)
+    pairs = None if wl.batch * wl.heads <= 16 else [(b, h) for b in (0, wl.batch - 1) for h in range(wl.heads)]
+    _compare_outputs(run, layers, rows_per_unit=64, bh=pairs)
+    if scas:
+        for l in layers:
+            _compare_scas(run, l, steps=range(min(wl.n_scales, 5)), heads=range(min(wl.heads, 4)),
+                          tol=1e-5 if wl.dtype == "f32" else SCAS_TOL)
+    check_cache(run, layers)
+    run.ctx.close()
+
+
+def test_fused_append_order_errors():
+    wl = _custom(73, "fused-errors", (1, 2, 3), heads=2, head_dim=128, batch=1, dtype="bf16")
+    keep = np.ones((1, 2, 3), dtype=np.uint8)
+    ctx = hk.Context(1, 2, 128, 1, wl.scale_tokens, keep, torch.bfloat16)
+    mk = lambda t: torch.zeros((1, wl.scale_tokens[t], 2, 128), dtype=torch.bfloat16, device="cuda")  # noqa
+    ctx.attend_append(0, 0, mk(0), mk(0), mk(0), mk(0), 1.0)
+    with pytest.raises(hk.HeatKVError) as e:          # scale 0 already appended
+        ctx.append_scale(0, 1, 0, mk(0), mk(0))
+    assert e.value.status == hk.HK_EORDER
+    ctx.attend(0, 1, mk(1), mk(1), mk(1), mk(1), 1.0)  # allowed: scale 0 is cached
+    ctx.append_scale(0, 1, 1, mk(1), mk(1))
+    with pytest.raises(hk.HeatKVError) as e:          # scale 1 appended twice
+        ctx.attend_append(0, 1, mk(1), mk(1), mk(1), mk(1), 1.0)
+    assert e.value.status == hk.HK_EORDER
+    ctx.attend_append(0, 2, mk(2), mk(2), mk(2), mk(2), 1.0)  # final scale: attention only
+    assert ctx.retained_tokens(2) == 2 * (1 + 4)
+    torch.cuda.synchronize()
+    ctx.close()
+
+
 def test_single_scale_workload():
     wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
     keep = np.zeros((1, 2, 1), dtype=np.uint8)

@@ -5,14 +5,20 @@
 //
 // A pure copy, bound by HBM bandwidth.  Each workgroup moves one block of
 // rows of one (segment, batch entry) for both K and V; every lane moves
-// 16-byte vectors, 16 lanes cover one 256-byte row, and each lane keeps
-// several loads in flight before storing.
+// 16-byte vectors, 16 lanes cover one 256-byte row, and each lane keeps eight
+// loads per tensor in flight before storing.  The cache is written with
+// nontemporal stores: the next reader is a later attend launch, so the lines
+// need not stay in the caches.  On the 32-layer batch-4 full-cache workload
+// this moves ~5.0 TB/s, against ~5.7 TB/s for the best plain contiguous copy
+// measured on the same chip.
 #include "device.h"
 
 namespace hk {
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kCopyThreads = 256;
-constexpr int kCopyItems = 4;   // 16-byte vectors per lane per tensor
+constexpr int kCopyItems = 8;   // 16-byte vectors per lane per tensor
 
 __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
   const int chunk = blockIdx.x % a.chunks;
@@ -32,15 +38,15 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
   const int64_t dst_row0 = d.dst + (int64_t(b) * d.cap + row0) * a.row_bytes;
 
   for (int base = threadIdx.x; base < items; base += kCopyThreads * kCopyItems) {
-    uint4 kv[kCopyItems], vv[kCopyItems];
+    u32x4 kv[kCopyItems], vv[kCopyItems];
 #pragma unroll
     for (int u = 0; u < kCopyItems; ++u) {
       const int it = base + u * kCopyThreads;
       if (it < items) {
         const int r = it / cpr, c = it % cpr;
         const int64_t off = src0 + r * tok_stride + c * 16;
-        kv[u] = *reinterpret_cast<const uint4*>(a.kcur + off);
-        vv[u] = *reinterpret_cast<const uint4*>(a.vcur + off);
+        kv[u] = *reinterpret_cast<const u32x4*>(a.kcur + off);
+        vv[u] = *reinterpret_cast<const u32x4*>(a.vcur + off);
       }
     }
 #pragma unroll
@@ -48,8 +54,8 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
       const int it = base + u * kCopyThreads;
       if (it < items) {
         const int64_t off = dst_row0 + int64_t(it) * 16;
-        *reinterpret_cast<uint4*>(a.kcache + off) = kv[u];
-        *reinterpret_cast<uint4*>(a.vcache + off) = vv[u];
+        __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(a.kcache + off));
+        __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(a.vcache + off));
       }
     }
   }

@@ -387,8 +387,8 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n = c->tokens[step];
     a.H = c->H;
     a.row_bytes = c->D * c->elem_bytes;
-    // 1024 16-byte vectors per tensor per workgroup: 4 per lane.
-    a.rows_per_block = std::min(std::max(1, 16384 / a.row_bytes), a.n);
+    // 2048 16-byte vectors per tensor per workgroup: 8 per lane.
+    a.rows_per_block = std::min(std::max(1, 32768 / a.row_bytes), a.n);
     a.chunks = (a.n + a.rows_per_block - 1) / a.rows_per_block;
     a.layer_begin = layer_begin;
     hipError_t e = hk::launch_compact(a, static_cast<hipStream_t>(hip_stream));

@@ -263,6 +263,10 @@ def main():
         result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
         result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
 
+    # ---------------- calibration: S-CAS cost and ranking stability ----------------
+    if not args.no_pruned:
+        result["calibration"] = calibration_rate(args, hk, workloads, torch, np, dev, stream)
+
     # ---------------- fp64 CPU oracle on a bounded sample ----------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, keep)
@@ -314,6 +318,77 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
             "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
             "passes": args.pruned_steps,
             "inputs": "torch.randn on the GPU (seeded), same distribution as the parity inputs"}
+
+
+def calibration_rate(args, hk, workloads, torch, np, dev, stream):
+    """Calibration workload (32 layers x 16 heads, batch 4, full cache, key
+    offsets per (head, source scale)): one pass with streamed S-CAS against the
+    same pass without, and the ranking stability between two calibration
+    subsets (two passes on different draws)."""
+    wl = workloads.get("c3")
+    keep = workloads.full_keep(wl)
+    K, L = wl.n_scales, wl.layers
+    mu = torch.from_numpy(workloads.key_offsets(wl)).to(dev)          # [H][K]
+    ctx = hk.Context(L, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep, torch.bfloat16)
+    outs = [torch.empty((wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim), dtype=torch.bfloat16,
+                        device=dev) for t in range(K)]
+
+    def draw(seed):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        qs, ks, vs = [], [], []
+        for t in range(K):
+            shape = (L, wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim)
+            qs.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+            z = torch.randn(shape, generator=g, device=dev) + mu[None, None, None, :, t, None]
+            ks.append((z * wl.qk_std).to(torch.bfloat16))
+            vs.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        return qs, ks, vs
+
+    def run(data, table):
+        qs, ks, vs = data
+        ctx.reset()
+        for t in range(K):
+            for l in range(L):
+                if table is None:
+                    ctx.attend(l, t, qs[t][l], ks[t][l], vs[t][l], outs[t], 1.0, stream=stream)
+                else:
+                    ctx.attend_with_scas_sum(l, t, qs[t][l], ks[t][l], vs[t][l], outs[t], 1.0, table,
+                                             stream=stream)
+            if t < K - 1:
+                ctx.append_scale(0, L, t, ks[t], vs[t], stream=stream)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    data = draw(11)
+    scratch = torch.zeros((L, wl.heads, K, K), dtype=torch.float64, device=dev)
+    ms_plain = timed(lambda: run(data, None), 2)
+    ms_scas = timed(lambda: run(data, scratch), 2)
+    tables = []
+    for seed in (21, 22):
+        tab = torch.zeros((L, wl.heads, K, K), dtype=torch.float64, device=dev)
+        run(draw(seed), tab)
+        torch.cuda.synchronize()
+        tables.append(hk.scas_mean(tab.cpu().numpy(), wl.batch))
+    rho, jac = hk.ranking_stability(tables[0], tables[1], wl.scale_tokens, 0.10, 2)
+    ctx.close()
+    return {"workload": "infinity2b-l32-b4-calibration: 32 layers x 16 heads, batch 4, full cache",
+            "ms_per_pass_attend": round(ms_plain, 3), "ms_per_pass_with_scas": round(ms_scas, 3),
+            "scas_overhead_ratio": round(ms_scas / ms_plain, 3),
+            "ranking_stability": {"subsets": "two batches of 4 images (different draws)",
+                                  "spearman_rho_per_source_scale": {s: round(float(r), 4) for s, r in enumerate(rho)
+                                                                    if not np.isnan(r)},
+                                  "jaccard_pruned_at_10pct": round(jac, 4)}}
 
 
 def compact_rate(args, hk, workloads, torch, np, dev, stream):

@@ -158,6 +158,42 @@ int hk_attend_with_scas(hk_ctx* ctx, int layer, int step, const void* q, const v
                         const void* v_cur, void* out, float softmax_scale,
                         float* scas_table, void* hip_stream);
 
+/* Streaming calibration: hk_attend_with_scas over one batch of calibration
+ * images, adding instead of overwriting.  For every head h and source s <=
+ * step, the per-image S-CAS (mass on source s averaged over the step's
+ * queries) summed over the batch's B images is added to
+ *   scas_sum[layer][h][step][s]   (device double [L][H][K][K]).
+ * Calling it for every (layer, step) of N batches and dividing by the N*B
+ * images (hk_scas_mean) gives the S-CAS table of the whole calibration set:
+ * a small offline calibration set is aggregated into one table (HeatKV
+ * project page, Method steps 1-2; Results: rankings stay stable with a small
+ * calibration set).  Each call's contribution is summed in a fixed order.
+ * Errors: as hk_attend_with_scas. */
+int hk_attend_with_scas_sum(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,
+                            const void* v_cur, void* out, float softmax_scale, double* scas_sum,
+                            void* hip_stream);
+
+/* scas_out = scas_sum / images, element by element (host arrays of L*H*K*K).
+ * Errors: HK_EINVAL (null, images <= 0). */
+int hk_scas_mean(int L, int H, int K, const double* scas_sum, double images, float* scas_out);
+
+/* Stability of the schedule's rankings between two S-CAS tables, e.g. from
+ * two disjoint calibration subsets (HeatKV project page, Results; Pith page
+ * of arXiv 2605.14877, Figure 6 caption: ranking stability across
+ * calibration runs).  The pages do not define the measure; two are given:
+ *   rho_out[s] (host double [K]): for each prunable source scale
+ *     s = n_sink..K-2, the Spearman rank correlation between the positions
+ *     of the L*H heads in the two orderings O_s (hk_build_schedule's
+ *     orderings, ties by flat index); NaN for the other scales and when
+ *     L*H < 2;
+ *   jaccard_out (host double): |G_a & G_b| / |G_a | G_b| of the pruned
+ *     (layer, head, scale) sets of the two keep-masks hk_build_schedule
+ *     builds at budget_frac (1 when both are empty).
+ * Errors: as hk_build_schedule. */
+int hk_ranking_stability(int L, int H, int K, const int32_t* scale_tokens, const float* scas_a,
+                         const float* scas_b, double budget_frac, int n_sink, double* rho_out,
+                         double* jaccard_out);
+
 /* hk_attend (or, with scas_table != NULL, hk_attend_with_scas) of scale
  * `step` in `layer`, followed by hk_append_scale of the same scale and layer,
  * for callers that run the two back to back.  With bf16 both happen in one

@@ -25,7 +25,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 import torch  # first: the library binds to the HIP runtime torch has loaded
 
-__all__ = ["HeatKVError", "build_schedule", "layout", "Context", "library_path", "DTYPES"]
+__all__ = ["HeatKVError", "build_schedule", "layout", "scas_mean", "ranking_stability", "Context",
+           "library_path", "DTYPES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libheatkv.so")
@@ -70,6 +71,9 @@ def _load():
         "hk_retained_tokens": ([P, I, P], I),
         "hk_attend_plan": ([P, I, I, P, P], I),
         "hk_attend_append": ([P, I, I, P, P, P, P, F, P, P], I),
+        "hk_attend_with_scas_sum": ([P, I, I, P, P, P, P, F, P, P], I),
+        "hk_scas_mean": ([I, I, I, P, D, P], I),
+        "hk_ranking_stability": ([I, I, I, P, P, P, D, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -122,6 +126,33 @@ def layout(scale_tokens: Sequence[int], keep: np.ndarray, batch: int,
     _check(_lib.hk_layout(L, H, K, _ptr(tok), _ptr(keep), int(batch), int(head_dim), _ptr(elems),
                           _ptr(cap), _ptr(base)))
     return int(elems[0]), cap, base
+
+
+def scas_mean(scas_sum: np.ndarray, images: float) -> np.ndarray:
+    """S-CAS table [L][H][K][K] float32 from a streamed double sum and the image count."""
+    scas_sum = np.ascontiguousarray(scas_sum, dtype=np.float64)
+    if scas_sum.ndim != 4:
+        raise HeatKVError(HK_EINVAL, "scas_sum must be [L][H][K][K]")
+    L, H, K, _ = scas_sum.shape
+    out = np.zeros(scas_sum.shape, dtype=np.float32)
+    _check(_lib.hk_scas_mean(L, H, K, _ptr(scas_sum), float(images), _ptr(out)))
+    return out
+
+
+def ranking_stability(scas_a: np.ndarray, scas_b: np.ndarray, scale_tokens: Sequence[int],
+                      budget_frac: float, n_sink: int) -> Tuple[np.ndarray, float]:
+    """(Spearman rho per source scale [K] (NaN where not prunable), Jaccard of pruned sets)."""
+    a = np.ascontiguousarray(scas_a, dtype=np.float32)
+    b = np.ascontiguousarray(scas_b, dtype=np.float32)
+    if a.shape != b.shape or a.ndim != 4:
+        raise HeatKVError(HK_EINVAL, "tables must both be [L][H][K][K]")
+    L, H, K, _ = a.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    rho = np.zeros(K, dtype=np.float64)
+    jac = np.zeros(1, dtype=np.float64)
+    _check(_lib.hk_ranking_stability(L, H, K, _ptr(tok), _ptr(a), _ptr(b), float(budget_frac),
+                                     int(n_sink), _ptr(rho), _ptr(jac)))
+    return rho, float(jac[0])
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -211,6 +242,20 @@ class Context:
         _check(_lib.hk_attend_with_scas(self._handle(), int(layer), int(step), *args,
                                         float(softmax_scale), ctypes.c_void_p(scas_table.data_ptr()),
                                         _stream(stream)))
+
+    def attend_with_scas_sum(self, layer: int, step: int, q, k, v, out, softmax_scale: float,
+                             scas_sum: torch.Tensor, stream=None) -> None:
+        """attend_with_scas, adding the batch's per-image S-CAS sum into a float64 table."""
+        if not (0 <= step < self.K):
+            raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+        args = [self._step_tensor(t, step, nm) for t, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out"))]
+        want = (self.L, self.H, self.K, self.K)
+        if (tuple(scas_sum.shape) != want or scas_sum.dtype != torch.float64
+                or scas_sum.device != self.device or not scas_sum.is_contiguous()):
+            raise HeatKVError(HK_EINVAL, f"scas_sum must be a contiguous float64 {want} device tensor")
+        _check(_lib.hk_attend_with_scas_sum(self._handle(), int(layer), int(step), *args,
+                                            float(softmax_scale), ctypes.c_void_p(scas_sum.data_ptr()),
+                                            _stream(stream)))
 
     def attend_append(self, layer: int, step: int, q, k, v, out, softmax_scale: float,
                       scas_table: Optional[torch.Tensor] = None, stream=None) -> None:

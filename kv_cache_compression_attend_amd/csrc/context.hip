@@ -104,11 +104,11 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
 
 int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
                   const void* v_cur, void* out, float softmax_scale, float* scas_table,
-                  bool scas, bool append, void* hip_stream) {
+                  bool scas, bool append, void* hip_stream, double* scas_sum = nullptr) {
   int rc = check_step_args(c, layer, step);
   if (rc != HK_OK) return rc;
   if (!q || !k_cur || !v_cur || !out) return fail(HK_EINVAL, "null tensor pointer");
-  if (scas && !scas_table) return fail(HK_EINVAL, "null S-CAS table");
+  if (scas && !scas_table && !scas_sum) return fail(HK_EINVAL, "null S-CAS table");
   if (!aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) || !aligned16(out))
     return fail(HK_EINVAL, "tensor pointers must be 16-byte aligned");
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale))
@@ -157,8 +157,10 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
                                            : hk::launch_attend_f32(a, c->D, scas, s);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   if (scas) {
-    e = hk::launch_scas_finalize(c->d_partials, scas_table, layer, c->H, c->K, c->B, a.n, step,
-                                 a.n_qtiles, s);
+    e = scas_sum ? hk::launch_scas_accumulate(c->d_partials, scas_sum, layer, c->H, c->K, c->B,
+                                              a.n, step, a.n_qtiles, s)
+                 : hk::launch_scas_finalize(c->d_partials, scas_table, layer, c->H, c->K, c->B,
+                                            a.n, step, a.n_qtiles, s);
     if (e != hipSuccess) return hip_fail(e, "S-CAS finalize launch");
   }
   if (append) {
@@ -331,6 +333,14 @@ extern "C" int hk_attend_with_scas(hk_ctx* c, int layer, int step, const void* q
                                    float softmax_scale, float* scas_table, void* hip_stream) {
   return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, scas_table, true, false,
                        hip_stream);
+}
+
+extern "C" int hk_attend_with_scas_sum(hk_ctx* c, int layer, int step, const void* q,
+                                       const void* k_cur, const void* v_cur, void* out,
+                                       float softmax_scale, double* scas_sum, void* hip_stream) {
+  if (!scas_sum) return fail(HK_EINVAL, "null S-CAS sum table");
+  return attend_common(c, layer, step, q, k_cur, v_cur, out, softmax_scale, nullptr, true, false,
+                       hip_stream, scas_sum);
 }
 
 extern "C" int hk_attend_append(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,

@@ -81,6 +81,8 @@ hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s
 hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
 hipError_t launch_scas_finalize(const float* partials, float* table, int layer, int H, int K,
                                 int B, int n, int step, int n_qtiles, hipStream_t s);
+hipError_t launch_scas_accumulate(const float* partials, double* table, int layer, int H, int K,
+                                  int B, int n, int step, int n_qtiles, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 
 }  // namespace hk

@@ -36,23 +36,51 @@ int fail(int code, const char* fmt, ...) {
 
 extern "C" const char* hk_last_error(void) { return hk::g_last_error.c_str(); }
 
-extern "C" int hk_build_schedule(int L, int H, int K, const int32_t* scale_tokens,
-                                 const float* scas, double budget_frac, int n_sink,
-                                 uint8_t* keep_out, int64_t* retained_out,
-                                 int32_t* n_pruned_out) {
-  using hk::fail;
+namespace {
+
+using hk::fail;
+
+int check_schedule_args(int L, int H, int K, const int32_t* scale_tokens, const void* scas,
+                        double budget_frac, int n_sink) {
   if (L < 1 || H < 1 || K < 1) return fail(HK_EINVAL, "L, H, K must be >= 1");
-  if (!scale_tokens || !scas || !keep_out) return fail(HK_EINVAL, "null argument");
+  if (!scale_tokens || !scas) return fail(HK_EINVAL, "null argument");
   for (int s = 0; s < K; ++s)
     if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
   if (n_sink < 0 || n_sink > K - 1) return fail(HK_EINVAL, "n_sink must be in [0, K-1]");
   if (!(budget_frac > 0.0 && budget_frac <= 1.0))
     return fail(HK_EINVAL, "budget_frac must be in (0, 1]");
+  return HK_OK;
+}
 
+// O_s: the flat head indices ascending by (importance, index), where the
+// importance of head f for source scale s is its S-CAS mass summed over the
+// later target scales t > s, in double, ascending t.
+void ordering(const float* scas, int64_t heads, int K, int s, std::vector<double>& imp,
+              std::vector<int64_t>& order) {
+  imp.assign(heads, 0.0);
+  for (int64_t f = 0; f < heads; ++f) {
+    double acc = 0.0;
+    for (int t = s + 1; t < K; ++t) acc += double(scas[(f * K + t) * K + s]);
+    imp[f] = acc;
+  }
+  order.resize(heads);
+  std::iota(order.begin(), order.end(), int64_t(0));
+  // Least dependent first; equal importance drops the lower flat index first.
+  std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
+    return imp[a] < imp[b] || (imp[a] == imp[b] && a < b);
+  });
+}
+
+}  // namespace
+
+extern "C" int hk_build_schedule(int L, int H, int K, const int32_t* scale_tokens,
+                                 const float* scas, double budget_frac, int n_sink,
+                                 uint8_t* keep_out, int64_t* retained_out,
+                                 int32_t* n_pruned_out) {
+  int rc = check_schedule_args(L, H, K, scale_tokens, scas, budget_frac, n_sink);
+  if (rc != HK_OK) return rc;
+  if (!keep_out) return fail(HK_EINVAL, "null argument");
   const int64_t heads = int64_t(L) * H;
-  const auto at = [&](int64_t f, int t, int s) -> double {
-    return double(scas[(f * K + t) * K + s]);
-  };
 
   // Token-slot costs per sequence.
   int64_t cached_tokens = 0, sink_tokens = 0, prunable_tokens = 0;
@@ -76,20 +104,10 @@ extern "C" int hk_build_schedule(int L, int H, int K, const int32_t* scale_token
     for (int s = 0; s < K; ++s) keep_out[f * K + s] = s <= K - 2 ? 1 : 0;
 
   if (n_prune > 0) {
-    std::vector<double> imp(heads);
-    std::vector<int64_t> order(heads);
+    std::vector<double> imp;
+    std::vector<int64_t> order;
     for (int s = n_sink; s <= K - 2; ++s) {
-      // Future dependence of each head on source scale s.
-      for (int64_t f = 0; f < heads; ++f) {
-        double acc = 0.0;
-        for (int t = s + 1; t < K; ++t) acc += at(f, t, s);
-        imp[f] = acc;
-      }
-      std::iota(order.begin(), order.end(), int64_t(0));
-      // Least dependent first; equal importance drops the lower flat index first.
-      std::sort(order.begin(), order.end(), [&](int64_t a, int64_t b) {
-        return imp[a] < imp[b] || (imp[a] == imp[b] && a < b);
-      });
+      ordering(scas, heads, K, s, imp, order);
       for (int64_t i = 0; i < n_prune; ++i) keep_out[order[i] * K + s] = 0;
     }
   }
@@ -106,6 +124,61 @@ extern "C" int hk_build_schedule(int L, int H, int K, const int32_t* scale_token
     }
   }
   if (n_pruned_out) *n_pruned_out = int32_t(n_prune);
+  return HK_OK;
+}
+
+extern "C" int hk_scas_mean(int L, int H, int K, const double* scas_sum, double images,
+                            float* scas_out) {
+  if (L < 1 || H < 1 || K < 1) return fail(HK_EINVAL, "L, H, K must be >= 1");
+  if (!scas_sum || !scas_out) return fail(HK_EINVAL, "null argument");
+  if (!(images > 0.0)) return fail(HK_EINVAL, "images must be positive");
+  const int64_t n = int64_t(L) * H * K * K;
+  for (int64_t i = 0; i < n; ++i) scas_out[i] = float(scas_sum[i] / images);
+  return HK_OK;
+}
+
+extern "C" int hk_ranking_stability(int L, int H, int K, const int32_t* scale_tokens,
+                                    const float* scas_a, const float* scas_b, double budget_frac,
+                                    int n_sink, double* rho_out, double* jaccard_out) {
+  int rc = check_schedule_args(L, H, K, scale_tokens, scas_a, budget_frac, n_sink);
+  if (rc != HK_OK) return rc;
+  if (!scas_b || !rho_out || !jaccard_out) return fail(HK_EINVAL, "null argument");
+  const int64_t heads = int64_t(L) * H;
+  std::vector<double> imp;
+  std::vector<int64_t> oa, ob, pos_a(heads), pos_b(heads);
+  for (int s = 0; s < K; ++s) {
+    rho_out[s] = std::nan("");
+    if (s < n_sink || s > K - 2 || heads < 2) continue;
+    ordering(scas_a, heads, K, s, imp, oa);
+    ordering(scas_b, heads, K, s, imp, ob);
+    for (int64_t i = 0; i < heads; ++i) {
+      pos_a[oa[i]] = i;
+      pos_b[ob[i]] = i;
+    }
+    // Spearman's rho of two permutations: 1 - 6 sum d^2 / (n (n^2 - 1)).
+    double d2 = 0.0;
+    for (int64_t f = 0; f < heads; ++f) {
+      const double d = double(pos_a[f] - pos_b[f]);
+      d2 += d * d;
+    }
+    const double n = double(heads);
+    rho_out[s] = 1.0 - 6.0 * d2 / (n * (n * n - 1.0));
+  }
+  std::vector<uint8_t> ka(heads * K), kb(heads * K);
+  rc = hk_build_schedule(L, H, K, scale_tokens, scas_a, budget_frac, n_sink, ka.data(), nullptr,
+                         nullptr);
+  if (rc != HK_OK) return rc;
+  rc = hk_build_schedule(L, H, K, scale_tokens, scas_b, budget_frac, n_sink, kb.data(), nullptr,
+                         nullptr);
+  if (rc != HK_OK) return rc;
+  int64_t inter = 0, uni = 0;
+  for (int64_t f = 0; f < heads; ++f)
+    for (int s = 0; s <= K - 2; ++s) {
+      const bool pa = !ka[f * K + s], pb = !kb[f * K + s];
+      inter += pa && pb;
+      uni += pa || pb;
+    }
+  *jaccard_out = uni == 0 ? 1.0 : double(inter) / double(uni);
   return HK_OK;
 }
 

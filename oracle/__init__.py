@@ -21,8 +21,10 @@ Modules:
              shared prefix, sink scales kept)
   cache      ragged cache layout, expected compacted contents, cache-size
              accounting
+  calibration  streamed S-CAS over many batches; ranking stability between
+             two calibration subsets
 
 Every function is written for readability, not speed.  Where the pages leave
 a step open, the reading taken is stated in the function's docstring.
 """
-from . import numerics, attention, schedule, cache  # noqa: F401
+from . import numerics, attention, schedule, cache, calibration  # noqa: F401

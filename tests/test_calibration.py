@@ -1,0 +1,84 @@
+"""Streaming calibration and ranking stability: oracle pins and the C ABI (CPU)."""
+import math
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import workloads
+from oracle import calibration as ocal
+from oracle import schedule as osch
+
+import kv_cache_compression_attend_amd as hk
+
+
+def test_streamed_mean_is_mean_over_images():
+    g = np.random.default_rng(0)
+    per_image = g.random((7, 2, 3, 4, 4))
+    sizes = [2, 4, 1]
+    tables, at = [], 0
+    for b in sizes:
+        tables.append(per_image[at:at + b].mean(axis=0))
+        at += b
+    np.testing.assert_allclose(ocal.streamed_mean(tables, sizes), per_image.mean(axis=0),
+                               rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_spearman_matches_library(seed):
+    g = np.random.default_rng(seed)
+    n = int(g.integers(2, 40))
+    pa, pb = g.permutation(n), g.permutation(n)
+    assert abs(ocal.spearman_positions(pa, pb) - stats.spearmanr(pa, pb).statistic) < 1e-12
+
+
+def test_stability_closed_forms():
+    t = workloads.random_scas_table(2, 3, 5, 1)
+    tok = (1, 4, 9, 16, 25)
+    rho, jac = ocal.ranking_stability(t, t, tok, 0.5, 1)
+    assert math.isnan(rho[0]) and math.isnan(rho[4])
+    assert np.all(rho[1:4] == 1.0) and jac == 1.0
+    # reversing every importance reverses every ordering (no ties): rho = -1
+    rev = np.zeros_like(t)
+    K = 5
+    for s in range(K):
+        for tt in range(s + 1, K):
+            rev[:, :, tt, s] = 1.0 - t[:, :, tt, s]
+    imp_t = osch.importance(t)
+    imp_r = osch.importance(rev)
+    ok = all(len(set(np.round(imp_t[:, :, s].ravel(), 9))) == 6 for s in range(1, 4))
+    assert ok
+    rho_r, _ = ocal.ranking_stability(t, rev, tok, 0.5, 1)
+    np.testing.assert_allclose(rho_r[1:4], -1.0, atol=1e-12)
+    assert np.allclose(imp_r[:, :, 1:4] + imp_t[:, :, 1:4], [[[3, 2, 1]]])
+
+
+def test_library_matches_oracle():
+    g = np.random.default_rng(3)
+    for i in range(200):
+        L, H, K = int(g.integers(1, 4)), int(g.integers(1, 6)), int(g.integers(2, 8))
+        tok = workloads.random_tokens(K, i)
+        a = workloads.random_scas_table(L, H, K, i)
+        b = workloads.random_scas_table(L, H, K, 1000 + i)
+        if i % 5 == 0:
+            b = a.copy()
+        beta = float(g.uniform(0.2, 1.0))
+        n_sink = int(g.integers(0, K))
+        try:
+            want = ocal.ranking_stability(a, b, tok, beta, n_sink)
+        except osch.ScheduleError:
+            with pytest.raises(hk.HeatKVError):
+                hk.ranking_stability(a, b, tok, beta, n_sink)
+            continue
+        rho, jac = hk.ranking_stability(a, b, tok, beta, n_sink)
+        np.testing.assert_array_equal(np.isnan(rho), np.isnan(want[0]))
+        np.testing.assert_allclose(rho[~np.isnan(rho)], want[0][~np.isnan(want[0])], rtol=0, atol=1e-12)
+        assert abs(jac - want[1]) < 1e-15
+
+
+def test_scas_mean_host():
+    g = np.random.default_rng(4)
+    s = g.random((2, 3, 4, 4))
+    np.testing.assert_array_equal(hk.scas_mean(s, 7.0), (s / 7.0).astype(np.float32))
+    with pytest.raises(hk.HeatKVError):
+        hk.scas_mean(s, 0.0)

@@ -219,6 +219,53 @@ def test_fused_append_order_errors():
     ctx.close()
 
 
+def test_streaming_calibration_over_batches():
+    """attend_with_scas_sum over three batches of calibration images, then the
+    mean over all images, equals the oracle's per-image S-CAS averaged over
+    every image of the three batches."""
+    wl = _custom(80, "calib-stream", (1, 2, 3, 5, 8), heads=4, head_dim=128, batch=2,
+                 dtype="bf16", layers=2)
+    keep = _random_keep(wl, 80)
+    K = wl.n_scales
+    total = torch.zeros((2, 4, K, K), dtype=torch.float64, device="cuda")
+    want = np.zeros((2, 4, K, K))
+    n_img = 0
+    for seed in (11, 12, 13):
+        ctx = hk.Context(2, 4, 128, 2, wl.scale_tokens, keep, torch.bfloat16)
+        ins = {l: [workloads.step_inputs(wl, l, t, seed) for t in range(K)] for l in range(2)}
+        for t in range(K):
+            for l in range(2):
+                x = ins[l][t]
+                q, k, v = to_device(x.q, wl), to_device(x.k, wl), to_device(x.v, wl)
+                out = torch.empty_like(q)
+                note(f"calib-stream seed {seed} layer {l} step {t}")
+                ctx.attend_with_scas_sum(l, t, q, k, v, out, 1.0, total)
+                if t < K - 1:
+                    ctx.append_scale(l, l + 1, t, k, v)
+        torch.cuda.synchronize()
+        ctx.close()
+        from oracle import attention as oatt
+        for l in range(2):
+            for t in range(K):
+                for h in range(4):
+                    for b in range(2):
+                        kj, vj, src, lens = oatt.gather_keys([x.k for x in ins[l][: t + 1]],
+                                                             [x.v for x in ins[l][: t + 1]], keep[l, h], t, b, h)
+                        _, p = oatt.softmax_attention(to_f64(ins[l][t].q[b, :, h, :], "bf16"),
+                                                      to_f64(kj, "bf16"), to_f64(vj, "bf16"), 1.0)
+                        want[l, h, t, : t + 1] += oatt.segment_mass(p, src, lens, t)
+        n_img += 2
+    got = hk.scas_mean(total.cpu().numpy(), n_img)
+    np.testing.assert_allclose(got, want / n_img, atol=SCAS_TOL, rtol=0)
+    for l in range(2):
+        for h in range(4):
+            for t in range(K):
+                np.testing.assert_allclose(got[l, h, t, : t + 1].sum(), 1.0, atol=1e-4)
+                for s in range(t):
+                    if not keep[l, h, s]:
+                        assert got[l, h, t, s] == 0.0
+
+
 def test_single_scale_workload():
     wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
     keep = np.zeros((1, 2, 1), dtype=np.uint8)

@@ -23,8 +23,10 @@ Modules:
              accounting
   calibration  streamed S-CAS over many batches; ranking stability between
              two calibration subsets
+  progressive  growing pruning sets (lazy prefix lengths N_k), cache size
+             after every layer, expiry steps and the cache contents they imply
 
 Every function is written for readability, not speed.  Where the pages leave
 a step open, the reading taken is stated in the function's docstring.
 """
-from . import numerics, attention, schedule, cache, calibration  # noqa: F401
+from . import numerics, attention, schedule, cache, calibration, progressive  # noqa: F401

@@ -114,6 +114,62 @@ int hk_build_schedule(int L, int H, int K, const int32_t* scale_tokens, const fl
 int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* keep,
               int B, int D, int64_t* cache_elems_out, int64_t* cap_out, int64_t* base_out);
 
+/* Progressive (lazy) schedule: the pruning set grows from scale to scale and
+ * segments of earlier scales are dropped from the middle of a head's cache
+ * when it does.
+ *
+ * Follows the Figure 4 caption of the Pith page of arXiv 2605.14877: after
+ * scale k the pruning set G_k is the union over scales i <= k of the prefix
+ * of length N_k of the ordering O_i, and must be absent by the end of scale
+ * k; and the signature of its Algorithm 2, CacheSizeAfterLayer(k, l, G_k,
+ * G_{k-1}, ...), which tracks the cache size layer by layer inside a scale.
+ * Readings taken:
+ *   orderings, prunable scales, sinks and the budget floor(budget_frac * F)
+ *     are those of hk_build_schedule;
+ *   N_k = the smallest N >= N_{k-1} for which the cache fits the budget
+ *     (greedy and lazy: nothing is pruned before the budget needs it);
+ *   with per_layer != 0 the budget must hold after every layer of scale k,
+ *     where layers 0..l hold their segments s <= k outside G_k and layers
+ *     l+1.. their segments s <= k-1 outside G_{k-1}; with per_layer == 0
+ *     only at the end of each scale.
+ *
+ *   expire_out   host uint8 [L][H][K]: expire[l][h][s] = the first k >= s
+ *                with (l, h, s) in G_k, else K-1 (kept to the end).  The
+ *                queries of scales t with s < t <= expire read segment s from
+ *                the cache; expire == s means it is never stored.
+ *   prefix_out   host int32 [K] or NULL: N_k (N_{K-1} = N_{K-2})
+ *   live_out     host int64 [K][L] or NULL: cache size in token slots per
+ *                sequence after layer l of scale k (row K-1 repeats the end
+ *                of scale K-2)
+ * Errors: as hk_build_schedule (HK_EBUDGET when the sink scales alone do not
+ * fit). */
+int hk_build_progressive_schedule(int L, int H, int K, const int32_t* scale_tokens,
+                                  const float* scas, double budget_frac, int n_sink,
+                                  int per_layer, uint8_t* expire_out, int32_t* prefix_out,
+                                  int64_t* live_out);
+
+/* Cache size, in token slots per sequence, once layer `layer` has finished
+ * scale `step` (the accounting of Algorithm 2 on the Pith page of arXiv
+ * 2605.14877, read as: layers 0..layer hold, per head, the segments s <=
+ * min(step, K-2) with expire > that bound; the later layers what they held at
+ * the end of step-1, nothing before step 0).
+ *   expire  host uint8 [L][H][K], each entry in [s, K-1]
+ * Errors: HK_EINVAL. */
+int hk_cache_size_after_layer(int L, int H, int K, const int32_t* scale_tokens,
+                              const uint8_t* expire, int step, int layer, int64_t* out);
+
+/* hk_layout for a schedule given as expiry steps (hk_layout(keep) equals
+ * this with expire = keep ? K-1 : s).  Head (l, h) gets the most rows it
+ * holds at the end of any scale:
+ *   cap[l][h] = max over k <= K-2 of the sum of n_s over s <= k with
+ *   expire[l][h][s] > k;
+ * at scale t rows [0, len) of (l, h, b) hold the segments s < t with
+ * expire >= t, in scale order.
+ * Errors: HK_EINVAL (also for an expire entry outside [s, K-1]). */
+int hk_layout_expiry(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* expire,
+                     int B, int D, int64_t* cache_elems_out, int64_t* cap_out,
+                     int64_t* base_out);
+
 /* Create a context on the current HIP device.  Copies scale_tokens and keep,
  * and uploads the small per-head tables.  k_cache / v_cache are caller-owned
  * device buffers of hk_layout() elements each; they must outlive the context.
@@ -122,6 +178,23 @@ int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* k
  * Errors: HK_EINVAL, HK_EUNSUPPORTED, HK_EHIP (allocation or copy failed). */
 int hk_create(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
               const uint8_t* keep, int dtype, void* k_cache, void* v_cache);
+
+/* hk_create for a schedule given as expiry steps (hk_build_progressive_schedule's
+ * output, or any table with entries in [s, K-1]); the cache buffers hold
+ * hk_layout_expiry() elements.  Scale t attends, per head, the held segments
+ * s < t with expire >= t.  hk_append_scale of scale t first moves the
+ * surviving segments down over those that expire at t (an in-place gather,
+ * one workgroup per (layer, head, batch entry), in ascending row order) and
+ * then stores segment t behind them.  Because the move and the store
+ * overwrite rows that scale t's attention reads, a layer where any head
+ * drops a segment at step t needs hk_attend (or hk_attend_with_scas) of
+ * (layer, t) before hk_append_scale of (layer, t), and no attend of (layer, t)
+ * after it, else HK_EORDER; hk_attend_append runs the two in that order
+ * (as separate launches at such steps).
+ * Errors: as hk_create. */
+int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
+                     const int32_t* scale_tokens, const uint8_t* expire, int dtype,
+                     void* k_cache, void* v_cache);
 
 /* Free the context's device tables (synchronises the device first). NULL is OK. */
 int hk_destroy(hk_ctx* ctx);

@@ -74,6 +74,10 @@ def _load():
         "hk_attend_with_scas_sum": ([P, I, I, P, P, P, P, F, P, P], I),
         "hk_scas_mean": ([I, I, I, P, D, P], I),
         "hk_ranking_stability": ([I, I, I, P, P, P, D, I, P, P], I),
+        "hk_build_progressive_schedule": ([I, I, I, P, P, D, I, I, P, P, P], I),
+        "hk_cache_size_after_layer": ([I, I, I, P, P, I, I, P], I),
+        "hk_layout_expiry": ([I, I, I, P, P, I, I, P, P, P], I),
+        "hk_create_expiry": ([P, I, I, I, I, I, P, P, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -128,6 +132,57 @@ def layout(scale_tokens: Sequence[int], keep: np.ndarray, batch: int,
     return int(elems[0]), cap, base
 
 
+def build_progressive_schedule(scas: np.ndarray, scale_tokens: Sequence[int], budget_frac: float,
+                               n_sink: int, per_layer: bool = True
+                               ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """S-CAS table + budget -> (expire u8 [L][H][K], prefix lengths N_k int32 [K],
+    cache size after each layer int64 [K][L])."""
+    scas = np.ascontiguousarray(scas, dtype=np.float32)
+    if scas.ndim != 4 or scas.shape[2] != scas.shape[3]:
+        raise HeatKVError(HK_EINVAL, "scas must be [L][H][K][K]")
+    L, H, K, _ = scas.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    expire = np.zeros((L, H, K), dtype=np.uint8)
+    prefix = np.zeros(K, dtype=np.int32)
+    live = np.zeros((K, L), dtype=np.int64)
+    _check(_lib.hk_build_progressive_schedule(L, H, K, _ptr(tok), _ptr(scas), float(budget_frac),
+                                              int(n_sink), int(bool(per_layer)), _ptr(expire),
+                                              _ptr(prefix), _ptr(live)))
+    return expire, prefix, live
+
+
+def cache_size_after_layer(scale_tokens: Sequence[int], expire: np.ndarray, step: int,
+                           layer: int) -> int:
+    """Token slots per sequence once ``layer`` has finished scale ``step``."""
+    expire = np.ascontiguousarray(expire, dtype=np.uint8)
+    L, H, K = expire.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    out = np.zeros(1, dtype=np.int64)
+    _check(_lib.hk_cache_size_after_layer(L, H, K, _ptr(tok), _ptr(expire), int(step), int(layer),
+                                          _ptr(out)))
+    return int(out[0])
+
+
+def layout_expiry(scale_tokens: Sequence[int], expire: np.ndarray, batch: int,
+                  head_dim: int) -> Tuple[int, np.ndarray, np.ndarray]:
+    """layout() for a schedule given as expiry steps."""
+    expire = np.ascontiguousarray(expire, dtype=np.uint8)
+    L, H, K = expire.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    elems = np.zeros(1, dtype=np.int64)
+    cap = np.zeros((L, H), dtype=np.int64)
+    base = np.zeros((L, H), dtype=np.int64)
+    _check(_lib.hk_layout_expiry(L, H, K, _ptr(tok), _ptr(expire), int(batch), int(head_dim),
+                                 _ptr(elems), _ptr(cap), _ptr(base)))
+    return int(elems[0]), cap, base
+
+
 def scas_mean(scas_sum: np.ndarray, images: float) -> np.ndarray:
     """S-CAS table [L][H][K][K] float32 from a streamed double sum and the image count."""
     scas_sum = np.ascontiguousarray(scas_sum, dtype=np.float64)
@@ -166,23 +221,32 @@ class Context:
 
     Allocates the two ragged caches (K and V) with PyTorch on the current
     device unless ``k_cache``/``v_cache`` are given, and keeps them alive for
-    the context's lifetime.
+    the context's lifetime.  The schedule is a static keep-mask ``keep``
+    [L][H][K], or expiry steps ``expire`` [L][H][K] (pass ``keep=None``).
     """
 
     def __init__(self, layers: int, heads: int, head_dim: int, batch: int,
-                 scale_tokens: Sequence[int], keep: np.ndarray, dtype: torch.dtype,
+                 scale_tokens: Sequence[int], keep: Optional[np.ndarray], dtype: torch.dtype,
                  k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
-                 device=None):
+                 device=None, expire: Optional[np.ndarray] = None):
         if dtype not in DTYPES:
             raise HeatKVError(HK_EUNSUPPORTED, f"dtype {dtype} not supported")
         self.L, self.H, self.D, self.B = int(layers), int(heads), int(head_dim), int(batch)
         self.tokens = tuple(int(x) for x in scale_tokens)
         self.K = len(self.tokens)
         self.dtype = dtype
-        self.keep = np.ascontiguousarray(keep, dtype=np.uint8)
-        if self.keep.shape != (self.L, self.H, self.K):
-            raise HeatKVError(HK_EINVAL, "keep must be [L][H][K]")
-        self.cache_elems, self.cap, self.base = layout(self.tokens, self.keep, self.B, self.D)
+        if (keep is None) == (expire is None):
+            raise HeatKVError(HK_EINVAL, "give exactly one of keep and expire")
+        sched = keep if expire is None else expire
+        self.keep = np.ascontiguousarray(keep, dtype=np.uint8) if expire is None else None
+        self.expire = np.ascontiguousarray(expire, dtype=np.uint8) if expire is not None else None
+        if np.asarray(sched).shape != (self.L, self.H, self.K):
+            raise HeatKVError(HK_EINVAL, "the schedule must be [L][H][K]")
+        if expire is None:
+            self.cache_elems, self.cap, self.base = layout(self.tokens, self.keep, self.B, self.D)
+        else:
+            self.cache_elems, self.cap, self.base = layout_expiry(self.tokens, self.expire, self.B,
+                                                                  self.D)
         dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
         n_alloc = max(self.cache_elems, 1)
         if k_cache is None:
@@ -197,11 +261,13 @@ class Context:
         self.device = k_cache.device
         tok = np.ascontiguousarray(self.tokens, dtype=np.int32)
         handle = ctypes.c_void_p()
+        create = _lib.hk_create if expire is None else _lib.hk_create_expiry
+        table = self.keep if expire is None else self.expire
         with torch.cuda.device(self.device):
-            _check(_lib.hk_create(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
-                                  _ptr(tok), _ptr(self.keep), DTYPES[dtype],
-                                  ctypes.c_void_p(k_cache.data_ptr()),
-                                  ctypes.c_void_p(v_cache.data_ptr())))
+            _check(create(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
+                          _ptr(tok), _ptr(table), DTYPES[dtype],
+                          ctypes.c_void_p(k_cache.data_ptr()),
+                          ctypes.c_void_p(v_cache.data_ptr())))
         self._h = handle
 
     # -- argument checks (shapes the kernels and their grids assume) -------------------

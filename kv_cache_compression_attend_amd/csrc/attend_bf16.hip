@@ -236,8 +236,10 @@ __device__ __forceinline__ Head setup(const AttendArgs& a) {
                     hd.Lc, hd.Ltot, hd.n, hd.tokb};
   hd.q = static_cast<const char*>(a.q) + curoff;
   // One workgroup per (b, h, split) appends: the one with q-tile 0.  A pruned
-  // segment (no cache rows reserved for this scale) is never written.
-  hd.append = a.append && hd.qt == 0 && a.step + 1 < a.K && hd.lenb[a.step + 1] > hd.Lc;
+  // segment (no cache rows reserved for this scale) is never written, and
+  // nothing is written past the head's capacity.
+  hd.append = a.append && hd.qt == 0 && a.step + 1 < a.K && hd.lenb[a.step + 1] > hd.Lc &&
+              hd.lenb[a.step + 1] <= cap;
   return hd;
 }
 

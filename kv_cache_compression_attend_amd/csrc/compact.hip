@@ -61,6 +61,65 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
   }
 }
 
+// In-place gather of one (layer, head, batch entry) cache region: the
+// segments that outlive the step move down over the dropped ones (Pith page
+// of arXiv 2605.14877, Figure 4 caption: a growing pruning set must be absent
+// by the end of its scale, so segments leave from the middle of the cache).
+//
+// Destination rows are rewritten in ascending chunks, one workgroup per
+// region.  Every destination row's source row lies at or above it, so within
+// a chunk all loads finish (barrier) before any store, and the loads of later
+// chunks start above every row stored so far: no byte is read after this
+// launch has written it, and no source byte is overwritten before it is read.
+__global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
+  __shared__ GatherRun runs[kMaxScales];
+  const GatherDesc d = a.desc[blockIdx.x];
+  if (threadIdx.x < unsigned(d.n_runs)) runs[threadIdx.x] = a.runs[d.run_first + threadIdx.x];
+  __syncthreads();
+
+  const int64_t region = d.base + int64_t(blockIdx.y) * d.cap * a.row_bytes;
+  uint8_t* kc = a.kcache + region;
+  uint8_t* vc = a.vcache + region;
+  const int cpr = a.row_bytes >> 4;
+  for (int row0 = d.dst_begin; row0 < d.dst_end; row0 += a.rows_per_chunk) {
+    const int items = min(a.rows_per_chunk, d.dst_end - row0) * cpr;
+    u32x4 kv[kCopyItems], vv[kCopyItems];
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      const int it = threadIdx.x + u * kCopyThreads;
+      if (it < items) {
+        const int row = row0 + it / cpr;
+        int src = row;
+        for (int r = 0; r < d.n_runs; ++r)
+          if (row < runs[r].dst + runs[r].rows) {
+            src = runs[r].src + (row - runs[r].dst);
+            break;
+          }
+        const int64_t off = int64_t(src) * a.row_bytes + (it % cpr) * 16;
+        kv[u] = *reinterpret_cast<const u32x4*>(kc + off);
+        vv[u] = *reinterpret_cast<const u32x4*>(vc + off);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      const int it = threadIdx.x + u * kCopyThreads;
+      if (it < items) {
+        const int64_t off = int64_t(row0) * a.row_bytes + int64_t(it) * 16;
+        __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(kc + off));
+        __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(vc + off));
+      }
+    }
+  }
+}
+
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
+  if (a.n_desc == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned(a.n_desc), unsigned(a.B)), dim3(kCopyThreads), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
   if (blocks == 0) return hipSuccess;

@@ -10,31 +10,42 @@
 
 #include "../../include/heatkv.h"
 #include "device.h"
+#include "layout.h"
 #include "status.h"
 
 struct hk_ctx {
   int L, H, D, B, K, dtype, device;
   int elem_bytes;
   std::vector<int32_t> tokens;
-  std::vector<uint8_t> keep;      // [L][H][K]
+  std::vector<uint8_t> expire;    // [L][H][K] step at whose end a segment leaves
   std::vector<int64_t> cap;       // [L][H]
   std::vector<int64_t> base;      // [L][H] element offsets
-  std::vector<int32_t> lenb;      // [L][H][K] rows cached before scale t
+  std::vector<int32_t> lenb;      // [K][L][H][K] segment start rows while step t is attended
   std::vector<int64_t> retained;  // [K]
-  // Compaction descriptors: for scale t, the kept (l, h) sorted by l; the
-  // ones of layer l are desc_first[t*(L+1)+l] .. desc_first[t*(L+1)+l+1].
+  // Compaction descriptors: for scale t, the (l, h) that store segment t,
+  // sorted by l; the ones of layer l are desc_first[t*(L+1)+l] ..
+  // desc_first[t*(L+1)+l+1].
   std::vector<int64_t> desc_first;
+  // Gather descriptors (heads whose held segments move at step t), indexed
+  // the same way, and whether any head of layer l drops a held segment at
+  // step t ([K][L]); a dropped tail segment moves nothing but still changes
+  // where segment t is stored.
+  std::vector<int64_t> gdesc_first;
+  std::vector<uint8_t> drops;
   void* kcache;
   void* vcache;
   int64_t* d_base = nullptr;
   int32_t* d_cap = nullptr;
   int32_t* d_lenb = nullptr;
   hk::CopyDesc* d_desc = nullptr;
+  hk::GatherDesc* d_gdesc = nullptr;
+  hk::GatherRun* d_gruns = nullptr;
   float* d_partials = nullptr;
   std::vector<int> splits;        // [K] key-range splits of each scale's attend launch
   float* d_ws_o = nullptr;        // split workspace: unnormalised outputs
   float2* d_ws_ml = nullptr;      // split workspace: (max, denominator)
   std::vector<int> appended;      // last scale appended per layer (-1: none)
+  std::vector<int> attended;      // last scale attended per layer (-1: none)
 };
 
 namespace {
@@ -66,6 +77,8 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_cap);
   (void)hipFree(c->d_lenb);
   (void)hipFree(c->d_desc);
+  (void)hipFree(c->d_gdesc);
+  (void)hipFree(c->d_gruns);
   (void)hipFree(c->d_partials);
   (void)hipFree(c->d_ws_o);
   (void)hipFree(c->d_ws_ml);
@@ -75,6 +88,8 @@ void free_tables(hk_ctx* c) {
   c->d_cap = nullptr;
   c->d_lenb = nullptr;
   c->d_desc = nullptr;
+  c->d_gdesc = nullptr;
+  c->d_gruns = nullptr;
   c->d_partials = nullptr;
 }
 
@@ -116,6 +131,12 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   if (step > 0 && c->appended[layer] < step - 1)
     return fail(HK_EORDER, "attend(layer %d, step %d) needs scale %d appended first (last: %d)",
                 layer, step, step - 1, c->appended[layer]);
+  // Segments that leave the cache at this step are overwritten by the
+  // append: once that has run, this step's layout is gone.
+  const bool drops = c->drops[int64_t(step) * c->L + layer] != 0;
+  if (drops && c->appended[layer] >= step)
+    return fail(HK_EORDER, "attend(layer %d, step %d) after its append: the cache no longer holds "
+                "the segments this step reads", layer, step);
   // Appending this scale as well needs the layer's cache to end at scale step-1.
   append = append && step <= c->K - 2;
   if (append && c->appended[layer] != step - 1)
@@ -135,7 +156,7 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.vcache = c->vcache;
   a.base = c->d_base + int64_t(layer) * c->H;
   a.cap = c->d_cap + int64_t(layer) * c->H;
-  a.lenb = c->d_lenb + int64_t(layer) * c->H * c->K;
+  a.lenb = c->d_lenb + (int64_t(step) * c->L + layer) * c->H * c->K;
   a.partials = c->d_partials;
   a.ws_o = c->d_ws_o;
   a.ws_ml = c->d_ws_ml;
@@ -149,13 +170,17 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.n_qtiles = (a.n + rows - 1) / rows;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
-  // bf16 kernels append in the same launch; the fp32 path runs the
-  // compaction kernel after the attention kernel.
-  a.append = append && c->dtype == HK_DTYPE_BF16;
+  // bf16 kernels append in the same launch, unless segments leave at this
+  // step (segment t is then stored where the attention still reads, after
+  // the survivors); otherwise the gather and compaction kernels run after the
+  // attention kernel.
+  const bool fused = append && c->dtype == HK_DTYPE_BF16 && !drops;
+  a.append = fused;
 
   hipError_t e = c->dtype == HK_DTYPE_BF16 ? hk::launch_attend_bf16_d128(a, scas, s)
                                            : hk::launch_attend_f32(a, c->D, scas, s);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
+  c->attended[layer] = step;
   if (scas) {
     e = scas_sum ? hk::launch_scas_accumulate(c->d_partials, scas_sum, layer, c->H, c->K, c->B,
                                               a.n, step, a.n_qtiles, s)
@@ -164,7 +189,7 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
     if (e != hipSuccess) return hip_fail(e, "S-CAS finalize launch");
   }
   if (append) {
-    if (c->dtype == HK_DTYPE_BF16) {
+    if (fused) {
       c->appended[layer] = step;
     } else {
       rc = append_launch(c, layer, layer + 1, step, k_cur, v_cur, 0, hip_stream);
@@ -176,14 +201,14 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
 
 }  // namespace
 
-extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
-                         const int32_t* scale_tokens, const uint8_t* keep, int dtype,
-                         void* k_cache, void* v_cache) {
+extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
+                                const int32_t* scale_tokens, const uint8_t* expire, int dtype,
+                                void* k_cache, void* v_cache) {
   if (!out) return fail(HK_EINVAL, "null output pointer");
   *out = nullptr;
   if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
   if (K > HK_MAX_SCALES) return fail(HK_EUNSUPPORTED, "K = %d exceeds %d scales", K, HK_MAX_SCALES);
-  if (!scale_tokens || !keep) return fail(HK_EINVAL, "null scale_tokens or keep");
+  if (!scale_tokens || !expire) return fail(HK_EINVAL, "null scale_tokens or schedule");
   if (dtype == HK_DTYPE_BF16) {
     if (D != 128) return fail(HK_EUNSUPPORTED, "bf16 needs head_dim 128 (got %d)", D);
   } else if (dtype == HK_DTYPE_F32) {
@@ -194,32 +219,28 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
   }
   for (int s = 0; s < K; ++s)
     if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+  const int64_t heads = int64_t(L) * H;
+  const int64_t bad = hk::first_bad_expire(expire, heads, K);
+  if (bad >= 0)
+    return fail(HK_EINVAL, "expire[%lld] = %d outside [scale, K-1]", (long long)bad, int(expire[bad]));
 
   auto* c = new hk_ctx();
   c->L = L; c->H = H; c->D = D; c->B = B; c->K = K; c->dtype = dtype;
   c->elem_bytes = dtype == HK_DTYPE_BF16 ? 2 : 4;
   c->tokens.assign(scale_tokens, scale_tokens + K);
-  c->keep.assign(keep, keep + int64_t(L) * H * K);
-  for (auto& v : c->keep) v = v ? 1 : 0;
+  c->expire.assign(expire, expire + heads * K);
   c->kcache = k_cache;
   c->vcache = v_cache;
   c->appended.assign(L, -1);
+  c->attended.assign(L, -1);
 
-  const int64_t heads = int64_t(L) * H;
-  c->cap.assign(heads, 0);
+  hk::step_tables(expire, scale_tokens, heads, K, c->lenb, c->cap);
   c->base.assign(heads, 0);
-  c->lenb.assign(heads * K, 0);
   int64_t offset = 0;
   for (int64_t f = 0; f < heads; ++f) {
-    int64_t run = 0;
-    for (int t = 0; t < K; ++t) {
-      c->lenb[f * K + t] = int32_t(run);
-      if (t <= K - 2 && c->keep[f * K + t]) run += scale_tokens[t];
-    }
-    if (run > INT32_MAX) { delete c; return fail(HK_EINVAL, "head cache exceeds 2^31 rows"); }
-    c->cap[f] = run;
+    if (c->cap[f] > INT32_MAX) { delete c; return fail(HK_EINVAL, "head cache exceeds 2^31 rows"); }
     c->base[f] = offset;
-    offset += run * B * D;
+    offset += c->cap[f] * B * D;
   }
   const int64_t cache_elems = offset;
   if (cache_elems > 0 && (!k_cache || !v_cache)) {
@@ -230,26 +251,46 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
     delete c;
     return fail(HK_EINVAL, "cache buffers must be 16-byte aligned");
   }
+  auto lenb_at = [&](int t, int64_t f, int s) { return c->lenb[(int64_t(t) * heads + f) * K + s]; };
 
   c->retained.assign(K, 0);
-  int64_t run = 0;
-  for (int k = 0; k < K; ++k) {
-    if (k <= K - 2)
-      for (int64_t f = 0; f < heads; ++f) run += c->keep[f * K + k] * int64_t(scale_tokens[k]);
-    c->retained[k] = run;
-  }
+  for (int k = 0; k < K; ++k)
+    for (int64_t f = 0; f < heads; ++f)
+      c->retained[k] += hk::rows_at_end(expire + f * K, scale_tokens, K, k);
 
+  // Per step: the heads that store segment t (at its row once the segments
+  // expiring at t are gone) and the heads whose held segments move.
   std::vector<hk::CopyDesc> desc;
+  std::vector<hk::GatherDesc> gdesc;
+  std::vector<hk::GatherRun> gruns;
+  std::vector<hk::MoveRun> runs;
   c->desc_first.assign(int64_t(K) * (L + 1), 0);
+  c->gdesc_first.assign(int64_t(K) * (L + 1), 0);
+  c->drops.assign(int64_t(K) * L, 0);
   for (int t = 0; t < K; ++t) {
     for (int l = 0; l < L; ++l) {
       c->desc_first[int64_t(t) * (L + 1) + l] = int64_t(desc.size());
+      c->gdesc_first[int64_t(t) * (L + 1) + l] = int64_t(gdesc.size());
       if (t > K - 2) continue;
       for (int h = 0; h < H; ++h) {
         const int64_t f = int64_t(l) * H + h;
-        if (!c->keep[f * K + t]) continue;
+        for (int sd = 0; sd < t; ++sd)
+          if (expire[f * K + sd] == t) c->drops[int64_t(t) * L + l] = 1;
+        hk::step_moves(expire + f * K, scale_tokens, K, t, runs);
+        if (!runs.empty()) {
+          hk::GatherDesc g{};
+          g.base = c->base[f] * c->elem_bytes;
+          g.cap = int32_t(c->cap[f]);
+          g.run_first = int32_t(gruns.size());
+          g.n_runs = int32_t(runs.size());
+          g.dst_begin = runs.front().dst;
+          g.dst_end = runs.back().dst + runs.back().rows;
+          for (const auto& r : runs) gruns.push_back(hk::GatherRun{r.dst, r.src, r.rows});
+          gdesc.push_back(g);
+        }
+        if (expire[f * K + t] <= t) continue;
         hk::CopyDesc d{};
-        d.dst = (c->base[f] + int64_t(c->lenb[f * K + t]) * D) * c->elem_bytes;
+        d.dst = (c->base[f] + int64_t(lenb_at(t + 1, f, t)) * D) * c->elem_bytes;
         d.cap = int32_t(c->cap[f]);
         d.head = h;
         d.layer = l;
@@ -257,6 +298,7 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
       }
     }
     c->desc_first[int64_t(t) * (L + 1) + L] = int64_t(desc.size());
+    c->gdesc_first[int64_t(t) * (L + 1) + L] = int64_t(gdesc.size());
   }
 
   int64_t max_partials = 1;
@@ -274,7 +316,7 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
     for (int t = 0; t < K; ++t) {
       int max_keys = 0;
       for (int64_t f = 0; f < heads; ++f)
-        max_keys = std::max<int>(max_keys, c->lenb[f * K + t] + scale_tokens[t]);
+        max_keys = std::max<int>(max_keys, lenb_at(t, f, t) + scale_tokens[t]);
       c->splits[t] = hk::attend_bf16_splits(B, H, scale_tokens[t], max_keys);
       if (c->splits[t] > 1)
         ws_rows = std::max<int64_t>(ws_rows, int64_t(c->splits[t]) * B * scale_tokens[t] * H);
@@ -287,6 +329,8 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
   if (e == hipSuccess) e = upload(&c->d_cap, cap32);
   if (e == hipSuccess) e = upload(&c->d_lenb, c->lenb);
   if (e == hipSuccess) e = upload(&c->d_desc, desc);
+  if (e == hipSuccess) e = upload(&c->d_gdesc, gdesc);
+  if (e == hipSuccess) e = upload(&c->d_gruns, gruns);
   if (e == hipSuccess)
     e = hipMalloc(reinterpret_cast<void**>(&c->d_partials),
                   size_t(max_partials) * hk::kMaxScales * sizeof(float));
@@ -301,6 +345,18 @@ extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
   }
   *out = c;
   return HK_OK;
+}
+
+extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
+                         const int32_t* scale_tokens, const uint8_t* keep, int dtype,
+                         void* k_cache, void* v_cache) {
+  if (!out) return fail(HK_EINVAL, "null output pointer");
+  *out = nullptr;
+  if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
+  if (!scale_tokens || !keep) return fail(HK_EINVAL, "null scale_tokens or keep");
+  std::vector<uint8_t> expire;
+  hk::expire_from_keep(keep, int64_t(L) * H, K, expire);
+  return hk_create_expiry(out, L, H, D, B, K, scale_tokens, expire.data(), dtype, k_cache, v_cache);
 }
 
 extern "C" int hk_destroy(hk_ctx* c) {
@@ -319,6 +375,7 @@ extern "C" int hk_destroy(hk_ctx* c) {
 extern "C" int hk_reset(hk_ctx* c) {
   if (!c) return fail(HK_EINVAL, "null context");
   c->appended.assign(c->L, -1);
+  c->attended.assign(c->L, -1);
   return HK_OK;
 }
 
@@ -365,10 +422,14 @@ extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int st
   if (nl > 1 && (layer_stride_elems < 0 ||
                  (layer_stride_elems * c->elem_bytes) % 16 != 0))
     return fail(HK_EINVAL, "layer stride must be non-negative and a multiple of 16 bytes");
-  for (int l = layer_begin; l < layer_end; ++l)
+  for (int l = layer_begin; l < layer_end; ++l) {
     if (c->appended[l] != step - 1)
       return fail(HK_EORDER, "append(layer %d, step %d) out of order (last appended: %d)", l,
                   step, c->appended[l]);
+    if (c->drops[int64_t(step) * c->L + l] && c->attended[l] != step)
+      return fail(HK_EORDER, "append(layer %d, step %d) overwrites segments that attend(layer %d, "
+                  "step %d) reads: attend first", l, step, l, step);
+  }
   return append_launch(c, layer_begin, layer_end, step, k_cur, v_cur, layer_stride_elems,
                        hip_stream);
 }
@@ -380,8 +441,26 @@ namespace {
 int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const void* k_cur,
                   const void* v_cur, int64_t layer_stride_elems, void* hip_stream) {
   const int nl = layer_end - layer_begin;
+  const int64_t gfirst = c->gdesc_first[int64_t(step) * (c->L + 1) + layer_begin];
+  const int64_t glast = c->gdesc_first[int64_t(step) * (c->L + 1) + layer_end];
   const int64_t first = c->desc_first[int64_t(step) * (c->L + 1) + layer_begin];
   const int64_t last = c->desc_first[int64_t(step) * (c->L + 1) + layer_end];
+  if (glast > gfirst) {
+    // Drop the segments that expire at this step before storing it.
+    DeviceGuard g(c->device);
+    if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+    hk::GatherArgs a{};
+    a.desc = c->d_gdesc + gfirst;
+    a.runs = c->d_gruns;
+    a.kcache = static_cast<uint8_t*>(c->kcache);
+    a.vcache = static_cast<uint8_t*>(c->vcache);
+    a.n_desc = int(glast - gfirst);
+    a.B = c->B;
+    a.row_bytes = c->D * c->elem_bytes;
+    a.rows_per_chunk = 32768 / a.row_bytes;  // 8 vectors per lane per tensor
+    hipError_t e = hk::launch_gather(a, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "gather launch");
+  }
   if (last > first) {
     DeviceGuard g(c->device);
     if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);

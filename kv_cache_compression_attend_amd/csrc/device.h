@@ -55,6 +55,34 @@ struct CompactArgs {
   int chunks;             // row blocks per (desc, b)
 };
 
+// One (layer, head) whose cache loses segments at a step: the held segments
+// that outlive the step move down over the dropped ones.  The moves are runs
+// (dst row, src row, rows) in ascending order with dst < src, covering
+// destination rows [dst_begin, dst_end) without gaps.
+struct GatherRun {
+  int32_t dst, src, rows;
+};
+
+struct GatherDesc {
+  int64_t base;           // byte offset of (l, h, b=0)'s region
+  int32_t cap;            // rows per batch entry of (l, h)
+  int32_t run_first;      // first run in the launch's run table
+  int32_t n_runs;         // <= kMaxScales
+  int32_t dst_begin;
+  int32_t dst_end;
+  int32_t pad;
+};
+
+struct GatherArgs {
+  const GatherDesc* desc;
+  const GatherRun* runs;
+  uint8_t* kcache;
+  uint8_t* vcache;
+  int n_desc, B;
+  int row_bytes;          // D * element size, a multiple of 16
+  int rows_per_chunk;     // rows moved per barrier interval
+};
+
 // Workgroups are handed to the 8 dies round-robin (workgroup i runs on die
 // i % 8).  This maps the hardware index to a logical index so that each die
 // receives one contiguous range of logical work, keeping a head's query tiles
@@ -84,5 +112,6 @@ hipError_t launch_scas_finalize(const float* partials, float* table, int layer, 
 hipError_t launch_scas_accumulate(const float* partials, double* table, int layer, int H, int K,
                                   int B, int n, int step, int n_qtiles, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
 }  // namespace hk

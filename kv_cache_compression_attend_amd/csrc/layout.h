@@ -1,0 +1,98 @@
+// Host-side cache layout of a schedule given as expiry steps.
+//
+// expire[f][s] (f = l*H + h) is the step at whose end segment s of head f
+// leaves the cache: the queries of scales t with s < t <= expire read it from
+// the cache, expire == s means it is never stored, expire == K-1 means it
+// stays to the end.  A static keep-mask is the case expire = K-1 (kept) or s
+// (pruned).  Pruning sets that grow from scale to scale (Pith page of arXiv
+// 2605.14877, Figure 4 caption: G_k is the union of prefixes of length N_k,
+// absent by the end of scale k) give expiry steps between s and K-1: the
+// segment is dropped from the middle of the head's cache at that step.
+#pragma once
+
+#include <algorithm>
+#include <cstdint>
+#include <vector>
+
+namespace hk {
+
+inline void expire_from_keep(const uint8_t* keep, int64_t heads, int K, std::vector<uint8_t>& out) {
+  out.resize(heads * K);
+  for (int64_t f = 0; f < heads; ++f)
+    for (int s = 0; s < K; ++s)
+      out[f * K + s] = uint8_t(keep[f * K + s] && s <= K - 2 ? K - 1 : s);
+}
+
+// Index of the first entry outside [s, K-1], or -1 when all are valid.
+inline int64_t first_bad_expire(const uint8_t* expire, int64_t heads, int K) {
+  for (int64_t f = 0; f < heads; ++f)
+    for (int s = 0; s < K; ++s)
+      if (expire[f * K + s] < s || expire[f * K + s] > K - 1) return f * K + s;
+  return -1;
+}
+
+// Rows of head f (per batch entry) at the end of step k; nothing changes
+// after step K-2 because the final scale is never cached.
+inline int64_t rows_at_end(const uint8_t* exp_f, const int32_t* tokens, int K, int k) {
+  const int kk = std::min(k, K - 2);
+  int64_t rows = 0;
+  for (int s = 0; s <= kk; ++s)
+    if (exp_f[s] > kk) rows += tokens[s];
+  return rows;
+}
+
+// lenb[(t*heads + f)*K + s]: first cache row of segment s while step t is
+// attended (segments s < t that are still held, in scale order); entry t is
+// the number of held rows, entry t+1 that plus n_t when segment t is stored
+// (equal to the rows at the end of step t when nothing leaves at t), later
+// entries repeat entry t+1.  cap[f] is the most rows head f holds at the end
+// of any step: segments leaving at step t are gone before segment t is
+// stored, so the two never occupy the cache together.
+inline void step_tables(const uint8_t* expire, const int32_t* tokens, int64_t heads, int K,
+                        std::vector<int32_t>& lenb, std::vector<int64_t>& cap) {
+  lenb.assign(int64_t(K) * heads * K, 0);
+  cap.assign(heads, 0);
+  for (int t = 0; t < K; ++t)
+    for (int64_t f = 0; f < heads; ++f) {
+      const uint8_t* e = expire + f * K;
+      int32_t* row = lenb.data() + (int64_t(t) * heads + f) * K;
+      int64_t run = 0;
+      for (int s = 0; s < K; ++s) {
+        row[s] = int32_t(run);
+        if (s < t && s <= K - 2 && e[s] >= t) run += tokens[s];
+        if (s == t && t <= K - 2 && e[t] > t) run += tokens[t];
+      }
+      cap[f] = std::max<int64_t>(cap[f], rows_at_end(e, tokens, K, t));
+    }
+}
+
+// Moves of step t for head f: the held segments that outlive step t, shifted
+// down over the segments that expire at t.  Consecutive surviving segments
+// with the same shift form one run (dst, src, rows), in ascending order.
+struct MoveRun {
+  int32_t dst, src, rows;
+};
+
+inline void step_moves(const uint8_t* exp_f, const int32_t* tokens, int K, int t,
+                       std::vector<MoveRun>& runs) {
+  runs.clear();
+  if (t > K - 2) return;
+  int32_t src = 0, dst = 0;
+  for (int s = 0; s < t; ++s) {
+    if (s > K - 2 || exp_f[s] < t) continue;  // not held at step t
+    const int32_t n = tokens[s];
+    if (exp_f[s] > t) {
+      if (dst != src) {
+        if (!runs.empty() && runs.back().src + runs.back().rows == src &&
+            runs.back().dst + runs.back().rows == dst)
+          runs.back().rows += n;
+        else
+          runs.push_back(MoveRun{dst, src, n});
+      }
+      dst += n;
+    }
+    src += n;
+  }
+}
+
+}  // namespace hk

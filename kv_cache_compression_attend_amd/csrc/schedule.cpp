@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/heatkv.h"
+#include "layout.h"
 #include "status.h"
 
 namespace hk {
@@ -182,23 +183,136 @@ extern "C" int hk_ranking_stability(int L, int H, int K, const int32_t* scale_to
   return HK_OK;
 }
 
+extern "C" int hk_layout_expiry(int L, int H, int K, const int32_t* scale_tokens,
+                                const uint8_t* expire, int B, int D, int64_t* cache_elems_out,
+                                int64_t* cap_out, int64_t* base_out) {
+  if (L < 1 || H < 1 || K < 1 || B < 1 || D < 1) return fail(HK_EINVAL, "sizes must be >= 1");
+  if (!scale_tokens || !expire || !cache_elems_out) return fail(HK_EINVAL, "null argument");
+  for (int s = 0; s < K; ++s)
+    if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+  const int64_t heads = int64_t(L) * H;
+  const int64_t bad = hk::first_bad_expire(expire, heads, K);
+  if (bad >= 0)
+    return fail(HK_EINVAL, "expire[%lld] = %d outside [scale, K-1]", (long long)bad, int(expire[bad]));
+  std::vector<int32_t> lenb;
+  std::vector<int64_t> cap;
+  hk::step_tables(expire, scale_tokens, heads, K, lenb, cap);
+  int64_t offset = 0;
+  for (int64_t f = 0; f < heads; ++f) {
+    if (cap_out) cap_out[f] = cap[f];
+    if (base_out) base_out[f] = offset;
+    offset += cap[f] * B * D;
+  }
+  *cache_elems_out = offset;
+  return HK_OK;
+}
+
 extern "C" int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* keep,
                          int B, int D, int64_t* cache_elems_out, int64_t* cap_out,
                          int64_t* base_out) {
-  using hk::fail;
   if (L < 1 || H < 1 || K < 1 || B < 1 || D < 1) return fail(HK_EINVAL, "sizes must be >= 1");
   if (!scale_tokens || !keep || !cache_elems_out) return fail(HK_EINVAL, "null argument");
-  int64_t offset = 0;
-  for (int64_t f = 0; f < int64_t(L) * H; ++f) {
-    int64_t cap = 0;
-    for (int s = 0; s <= K - 2; ++s) {
-      if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
-      if (keep[f * K + s]) cap += scale_tokens[s];
-    }
-    if (cap_out) cap_out[f] = cap;
-    if (base_out) base_out[f] = offset;
-    offset += cap * B * D;
+  std::vector<uint8_t> expire;
+  hk::expire_from_keep(keep, int64_t(L) * H, K, expire);
+  return hk_layout_expiry(L, H, K, scale_tokens, expire.data(), B, D, cache_elems_out, cap_out,
+                          base_out);
+}
+
+extern "C" int hk_cache_size_after_layer(int L, int H, int K, const int32_t* scale_tokens,
+                                         const uint8_t* expire, int step, int layer,
+                                         int64_t* out) {
+  if (L < 1 || H < 1 || K < 1) return fail(HK_EINVAL, "L, H, K must be >= 1");
+  if (!scale_tokens || !expire || !out) return fail(HK_EINVAL, "null argument");
+  if (step < 0 || step >= K) return fail(HK_EINVAL, "step %d out of [0, %d)", step, K);
+  if (layer < 0 || layer >= L) return fail(HK_EINVAL, "layer %d out of [0, %d)", layer, L);
+  const int64_t heads = int64_t(L) * H;
+  const int64_t bad = hk::first_bad_expire(expire, heads, K);
+  if (bad >= 0)
+    return fail(HK_EINVAL, "expire[%lld] = %d outside [scale, K-1]", (long long)bad, int(expire[bad]));
+  // Layers up to `layer` have finished the step; the later ones still hold
+  // what they held at the end of the previous step.
+  int64_t total = 0;
+  for (int64_t f = 0; f < heads; ++f) {
+    const bool done = f / H <= layer;
+    if (done) total += hk::rows_at_end(expire + f * K, scale_tokens, K, step);
+    else if (step > 0) total += hk::rows_at_end(expire + f * K, scale_tokens, K, step - 1);
   }
-  *cache_elems_out = offset;
+  *out = total;
+  return HK_OK;
+}
+
+extern "C" int hk_build_progressive_schedule(int L, int H, int K, const int32_t* scale_tokens,
+                                             const float* scas, double budget_frac, int n_sink,
+                                             int per_layer, uint8_t* expire_out,
+                                             int32_t* prefix_out, int64_t* live_out) {
+  int rc = check_schedule_args(L, H, K, scale_tokens, scas, budget_frac, n_sink);
+  if (rc != HK_OK) return rc;
+  if (!expire_out) return fail(HK_EINVAL, "null argument");
+  const int64_t heads = int64_t(L) * H;
+  int64_t cached_tokens = 0;
+  for (int s = 0; s <= K - 2; ++s) cached_tokens += scale_tokens[s];
+  const int64_t budget = int64_t(std::floor(budget_frac * double(heads * cached_tokens)));
+
+  // Orderings of the prunable scales n_sink..K-2.
+  std::vector<std::vector<int64_t>> orders(K);
+  {
+    std::vector<double> imp;
+    for (int s = n_sink; s <= K - 2; ++s) ordering(scas, heads, K, s, imp, orders[s]);
+  }
+  for (int64_t i = 0; i < heads * K; ++i) expire_out[i] = uint8_t(K - 1);
+  std::vector<uint8_t> pruned(heads * K, 0);
+  std::vector<int64_t> pending(L, 0), done(L, 0), sizes(L, 0);
+  int64_t n = 0;
+  for (int k = 0; k <= K - 2; ++k) {
+    // Start of step k: every layer holds its end-of-(k-1) rows; the prefix of
+    // O_k at the current length is pruned before segment k is ever stored.
+    if (k >= n_sink)
+      for (int64_t i = 0; i < n; ++i) pruned[orders[k][i] * K + k] = 1;
+    for (int l = 0; l < L; ++l) {
+      done[l] = pending[l];
+      for (int h = 0; h < H; ++h)
+        if (!pruned[(int64_t(l) * H + h) * K + k]) done[l] += scale_tokens[k];
+    }
+    for (;;) {
+      // Size after layer l: layers 0..l finished, the rest still pending.
+      int64_t total_pending = 0;
+      for (int l = 0; l < L; ++l) total_pending += pending[l];
+      int64_t run_done = 0, run_pending = total_pending, worst = 0;
+      for (int l = 0; l < L; ++l) {
+        run_done += done[l];
+        run_pending -= pending[l];
+        sizes[l] = run_done + run_pending;
+        worst = std::max(worst, sizes[l]);
+      }
+      if ((per_layer ? worst : sizes[L - 1]) <= budget) break;
+      if (n == heads)
+        return fail(HK_EBUDGET, "budget of %lld token slots cannot hold scale %d",
+                    (long long)budget, k);
+      // Grow the prefix by one: the next head of every ordering i <= k.
+      for (int i = n_sink; i <= k; ++i) {
+        const int64_t f = orders[i][n];
+        if (pruned[f * K + i]) continue;
+        pruned[f * K + i] = 1;
+        done[f / H] -= scale_tokens[i];
+      }
+      ++n;
+    }
+    for (int64_t f = 0; f < heads; ++f)
+      for (int i = 0; i <= k; ++i)
+        if (pruned[f * K + i] && expire_out[f * K + i] == K - 1) expire_out[f * K + i] = uint8_t(k);
+    if (prefix_out) prefix_out[k] = int32_t(n);
+    if (live_out)
+      for (int l = 0; l < L; ++l) live_out[int64_t(k) * L + l] = sizes[l];
+    pending = done;
+  }
+  if (K >= 2) {
+    if (prefix_out) prefix_out[K - 1] = int32_t(n);
+    if (live_out)
+      for (int l = 0; l < L; ++l) live_out[int64_t(K - 1) * L + l] = sizes[L - 1];
+  } else {
+    if (prefix_out) prefix_out[0] = 0;
+    if (live_out)
+      for (int l = 0; l < L; ++l) live_out[l] = 0;
+  }
   return HK_OK;
 }

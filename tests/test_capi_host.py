@@ -8,6 +8,7 @@ import pytest
 
 import workloads
 from oracle import cache as ocache
+from oracle import progressive as opr
 from oracle import schedule as osch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -31,7 +32,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -136,3 +137,88 @@ def test_null_and_range_errors_without_gpu():
                          None, None) == hk.HK_EINVAL
     assert lib.hk_create(ctypes.byref(h), 1, 1, 16, 1, 2, p(tok), p(keep), hk.HK_DTYPE_F32,
                          None, None) == hk.HK_EINVAL  # null cache with a non-empty layout
+
+
+def _progressive_same(table, tokens, beta, n_sink, per_layer):
+    try:
+        want = opr.progressive_schedule(table, tokens, beta, n_sink, per_layer)
+    except osch.ScheduleError as e:
+        with pytest.raises(hk.HeatKVError) as got:
+            hk.build_progressive_schedule(table, tokens, beta, n_sink, per_layer)
+        assert got.value.name == e.code.upper()
+        return None
+    exp, n, live = hk.build_progressive_schedule(table, tokens, beta, n_sink, per_layer)
+    np.testing.assert_array_equal(exp, want[0])
+    np.testing.assert_array_equal(n, want[1])
+    np.testing.assert_array_equal(live, want[2])
+    return exp
+
+
+def test_progressive_schedule_bit_exact_random_tables():
+    g = np.random.default_rng(11)
+    for i in range(400):
+        L, H, K = int(g.integers(1, 4)), int(g.integers(1, 5)), int(g.integers(1, 8))
+        tokens = workloads.random_tokens(K, 500 + i, max_side=5)
+        table = workloads.random_scas_table(L, H, K, 500 + i)
+        if i % 7 == 0:
+            table[:, :, :, :] = np.round(table * 4) / 4
+        beta = float(g.choice([g.uniform(0.01, 1.0), 1.0, 0.3]))
+        n_sink = int(g.integers(0, K))
+        exp = _progressive_same(table, tokens, beta, n_sink, bool(i % 2))
+        if exp is None:
+            continue
+        L, H, K = exp.shape
+        for k in range(K):
+            for l in range(L):
+                want = sum(opr.rows_at_end(exp[ll, h], tokens, k if ll <= l else k - 1)
+                           for ll in range(L) for h in range(H) if ll <= l or k > 0)
+                assert hk.cache_size_after_layer(tokens, exp, k, l) == want
+
+
+@pytest.mark.parametrize("key", ["c2", "c4"])
+def test_progressive_schedule_bit_exact_on_workload_tables(key):
+    wl = workloads.get(key)
+    table = workloads.dirichlet_scas(wl)
+    exp = _progressive_same(table, wl.scale_tokens, wl.budget, wl.n_sink, True)
+    elems, cap, base = hk.layout_expiry(wl.scale_tokens, exp, wl.batch, wl.head_dim)
+    ocap = opr.capacity(exp, wl.scale_tokens)
+    np.testing.assert_array_equal(cap, ocap)
+    np.testing.assert_array_equal(base, ocache.bases(ocap, wl.batch, wl.head_dim))
+    assert elems == int(ocap.sum()) * wl.batch * wl.head_dim
+
+
+def test_layout_of_keep_equals_layout_of_its_expiry():
+    wl = workloads.get("c2")
+    keep = osch.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, wl.budget, wl.n_sink)[0]
+    a = hk.layout(wl.scale_tokens, keep, wl.batch, wl.head_dim)
+    b = hk.layout_expiry(wl.scale_tokens, opr.expire_from_keep(keep), wl.batch, wl.head_dim)
+    assert a[0] == b[0]
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+
+
+def test_expiry_errors():
+    tok = (1, 4, 9)
+    bad = np.array([[[0, 2, 2]]], dtype=np.uint8)  # segment 0 leaves at step 0: fine
+    assert hk.cache_size_after_layer(tok, bad, 1, 0) == 4
+    for wrong in ([[[0, 0, 2]]], [[[3, 2, 2]]], [[[0, 1, 1]]]):
+        e_ = np.array(wrong, dtype=np.uint8)
+        with pytest.raises(hk.HeatKVError) as e:
+            hk.layout_expiry(tok, e_, 1, 16)
+        assert e.value.status == hk.HK_EINVAL
+        with pytest.raises(hk.HeatKVError) as e:
+            hk.cache_size_after_layer(tok, e_, 0, 0)
+        assert e.value.status == hk.HK_EINVAL
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.cache_size_after_layer(tok, bad, 3, 0)
+    assert e.value.status == hk.HK_EINVAL
+    lib = hk._lib
+    h = ctypes.c_void_p()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    wrong = np.array([[[0, 0, 2]]], dtype=np.uint8)
+    assert lib.hk_create_expiry(ctypes.byref(h), 1, 1, 16, 1, 3, p(np.array(tok, np.int32)), p(wrong),
+                                hk.HK_DTYPE_F32, None, None) == hk.HK_EINVAL
+    t = workloads.random_scas_table(1, 2, 4, 3)
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.build_progressive_schedule(t, (1, 4, 9, 16), 0.01, 1)
+    assert e.value.status == hk.HK_EBUDGET

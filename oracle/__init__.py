@@ -25,8 +25,10 @@ Modules:
              two calibration subsets
   progressive  growing pruning sets (lazy prefix lengths N_k), cache size
              after every layer, expiry steps and the cache contents they imply
+  policies   condensed + local scale-window schedule (a second generator of
+             expiry steps)
 
 Every function is written for readability, not speed.  Where the pages leave
 a step open, the reading taken is stated in the function's docstring.
 """
-from . import numerics, attention, schedule, cache, calibration, progressive  # noqa: F401
+from . import numerics, attention, schedule, cache, calibration, progressive, policies  # noqa: F401

@@ -261,6 +261,8 @@ def main():
     # ---------------- 32 layers, batch 8, 10% budget: scales/s per image ----------------
     if not args.no_pruned:
         result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
+        result["progressive_10pct"] = progressive_rate(args, hk, workloads, torch, np, dev, stream)
+        result["scale_window"] = window_rate(args, hk, workloads, torch, np, dev, stream)
         result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
 
     # ---------------- calibration: S-CAS cost and ranking stability ----------------
@@ -318,6 +320,138 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
             "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
             "passes": args.pruned_steps,
             "inputs": "torch.randn on the GPU (seeded), same distribution as the parity inputs"}
+
+
+def held_table(expire, tokens):
+    """Rows each (l, h) holds while step t is attended: held segments s < t."""
+    import numpy as np
+    L, H, K = expire.shape
+
+    def f(t):
+        out = np.zeros((L, H), dtype=np.int64)
+        for s in range(min(t, K - 1)):
+            out += (expire[:, :, s].astype(np.int64) >= t) * tokens[s]
+        return out
+    return f
+
+
+def moved_rows(expire, tokens, t):
+    """Rows per batch entry the gather of step t rewrites, summed over heads:
+    the surviving held segments behind the first one that leaves."""
+    L, H, K = expire.shape
+    total = 0
+    if t > K - 2:
+        return 0
+    for l in range(L):
+        for h in range(H):
+            e = expire[l, h]
+            seen_drop = False
+            for s in range(t):
+                if e[s] < t:
+                    continue
+                if e[s] == t:
+                    seen_drop = True
+                elif seen_drop:
+                    total += tokens[s]
+    return total
+
+
+def progressive_rate(args, hk, workloads, torch, np, dev, stream):
+    """Whole-pass rate of the 32-layer, batch-8, 10%-budget workload under the
+    progressive schedule (lazy prefix lengths, per-layer accounting): segments
+    stay cached until the budget needs their room and then leave from the
+    middle of the head's cache."""
+    wl = workloads.get("c2")
+    table = workloads.dirichlet_scas(wl)
+    expire, prefix, live = hk.build_progressive_schedule(table, wl.scale_tokens, wl.budget,
+                                                         wl.n_sink, True)
+    keep, _, _ = hk.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
+    K = wl.n_scales
+    flops = pass_flops(wl, None, held_table(expire, wl.scale_tokens))
+    static_flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
+    ms, elems = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3)
+    row_bytes = wl.head_dim * 2
+    gather_bytes = sum(moved_rows(expire, wl.scale_tokens, t) for t in range(K)) * wl.batch \
+        * row_bytes * 2 * 2
+    slot_bytes = wl.batch * row_bytes * 2          # one token slot of K and V, whole batch
+    budget_slots = int(np.floor(wl.budget * wl.layers * wl.heads * sum(wl.scale_tokens[: K - 1])))
+    return {"workload": "infinity2b-l32-b8-budget10-progressive: 32 layers x 16 heads x d128, "
+                        "batch 8, 10% budget, lazy prefix lengths with per-layer accounting",
+            "prefix_per_step": [int(x) for x in prefix],
+            "ms_per_pass": round(ms, 3),
+            "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
+            "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+            "attend_flops_vs_static": round(sum(flops.values()) / sum(static_flops.values()), 3),
+            "gather_bytes_per_pass": float(gather_bytes),
+            "live_peak_token_slots": int(live.max()),
+            "budget_token_slots": budget_slots,
+            "live_peak_GB": round(int(live.max()) * slot_bytes / 1e9, 3),
+            "allocated_cache_GB": round(elems * 2 * 2 / 1e9, 3),
+            "static_allocated_cache_GB": round(hk.layout(wl.scale_tokens, keep, wl.batch,
+                                                         wl.head_dim)[0] * 2 * 2 / 1e9, 3),
+            "passes": args.pruned_steps}
+
+
+def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed):
+    """Mean time of whole passes (every layer and scale, attend_append) under
+    an expiry schedule, on seeded GPU inputs of the workload's shapes."""
+    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, None,
+                     torch.bfloat16, expire=expire)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    K, L = wl.n_scales, wl.layers
+    qs, kall, vall, outs = [], [], [], []
+    for t in range(K):
+        shape = (L, wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim)
+        qs.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        kall.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        vall.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        outs.append(torch.empty(shape[1:], dtype=torch.bfloat16, device=dev))
+
+    def one_pass():
+        ctx.reset()
+        for t in range(K):
+            for l in range(L):
+                ctx.attend_append(l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                                  stream=stream)
+
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.pruned_steps):
+        one_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.pruned_steps
+    elems = ctx.cache_elems
+    ctx.close()
+    return ms, elems
+
+
+def window_rate(args, hk, workloads, torch, np, dev, stream):
+    """The 32-layer, batch-8 workload under the condensed + local scale-window
+    schedule: two condensed scales, a window of two local scales, and the four
+    layers with the lowest (seeded, synthetic) similarity score keep every
+    scale."""
+    wl = workloads.get("c2")
+    K, L = wl.n_scales, wl.layers
+    sim = np.random.default_rng(5).random(L).astype(np.float32)
+    expire = hk.build_scale_window_schedule(L, wl.heads, wl.scale_tokens, 2, 2, K, sim, 4)
+    ms, elems = expiry_pass(args, hk, wl, expire, torch, dev, stream, 4)
+    full = L * wl.heads * sum(wl.scale_tokens[: K - 1])
+    peak = max(hk.cache_size_after_layer(wl.scale_tokens, expire, k, l)
+               for k in range(K) for l in range(L))
+    flops = pass_flops(wl, None, held_table(expire, wl.scale_tokens))
+    return {"workload": "infinity2b-l32-b8-scale-window: 32 layers x 16 heads x d128, batch 8; "
+                        "2 condensed scales, 2 local scales, 4 cache-demanding layers keep all",
+            "ms_per_pass": round(ms, 3),
+            "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
+            "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+            "live_peak_fraction_of_full_cache": round(peak / full, 4),
+            "allocated_cache_GB": round(elems * 2 * 2 / 1e9, 3),
+            "passes": args.pruned_steps}
 
 
 def calibration_rate(args, hk, workloads, torch, np, dev, stream):

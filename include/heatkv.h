@@ -158,6 +158,24 @@ int hk_build_progressive_schedule(int L, int H, int K, const int32_t* scale_toke
 int hk_cache_size_after_layer(int L, int H, int K, const int32_t* scale_tokens,
                               const uint8_t* expire, int step, int layer, int64_t* out);
 
+/* A second schedule generator: condensed plus local scales, as expiry steps
+ * for hk_create_expiry (the AMS-KV paper's abstract: tokens of local scales
+ * matter most, a little memory for the coarsest, condensed, scales
+ * stabilises generation, and layers with weak inter-scale key/value
+ * similarity are cache-demanding and get more).  Readings taken:
+ *   scales 0..n_condensed-1 stay cached to the end (expire = K-1);
+ *   any other segment s is read by the next w scales and leaves at step
+ *     min(s + w, K-1), with w = window_demanding in the n_demanding layers
+ *     of lowest similarity[l] (ties: lower layer first), else w = window;
+ *   every head of a layer gets the same schedule.
+ *   similarity  host float [L], or NULL when n_demanding = 0
+ *   expire_out  host uint8 [L][H][K]
+ * Errors: HK_EINVAL. */
+int hk_build_scale_window_schedule(int L, int H, int K, const int32_t* scale_tokens,
+                                   int n_condensed, int window, int window_demanding,
+                                   const float* similarity, int n_demanding,
+                                   uint8_t* expire_out);
+
 /* hk_layout for a schedule given as expiry steps (hk_layout(keep) equals
  * this with expire = keep ? K-1 : s).  Head (l, h) gets the most rows it
  * holds at the end of any scale:

@@ -78,6 +78,7 @@ def _load():
         "hk_cache_size_after_layer": ([I, I, I, P, P, I, I, P], I),
         "hk_layout_expiry": ([I, I, I, P, P, I, I, P, P, P], I),
         "hk_create_expiry": ([P, I, I, I, I, I, P, P, I, P, P], I),
+        "hk_build_scale_window_schedule": ([I, I, I, P, I, I, I, P, I, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -151,6 +152,27 @@ def build_progressive_schedule(scas: np.ndarray, scale_tokens: Sequence[int], bu
                                               int(n_sink), int(bool(per_layer)), _ptr(expire),
                                               _ptr(prefix), _ptr(live)))
     return expire, prefix, live
+
+
+def build_scale_window_schedule(layers: int, heads: int, scale_tokens: Sequence[int],
+                                n_condensed: int, window: int, window_demanding: int,
+                                similarity: Optional[Sequence[float]] = None,
+                                n_demanding: int = 0) -> np.ndarray:
+    """Condensed + local scale-window policy -> expire u8 [L][H][K]."""
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    K = int(tok.shape[0])
+    sim = None
+    if similarity is not None:
+        sim = np.ascontiguousarray(similarity, dtype=np.float32)
+        if sim.shape != (int(layers),):
+            raise HeatKVError(HK_EINVAL, "similarity must have one score per layer")
+    expire = np.zeros((int(layers), int(heads), K), dtype=np.uint8)
+    _check(_lib.hk_build_scale_window_schedule(int(layers), int(heads), K, _ptr(tok),
+                                               int(n_condensed), int(window),
+                                               int(window_demanding),
+                                               _ptr(sim) if sim is not None else None,
+                                               int(n_demanding), _ptr(expire)))
+    return expire
 
 
 def cache_size_after_layer(scale_tokens: Sequence[int], expire: np.ndarray, step: int,

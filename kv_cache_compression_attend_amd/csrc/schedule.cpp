@@ -316,3 +316,37 @@ extern "C" int hk_build_progressive_schedule(int L, int H, int K, const int32_t*
   }
   return HK_OK;
 }
+
+extern "C" int hk_build_scale_window_schedule(int L, int H, int K, const int32_t* scale_tokens,
+                                              int n_condensed, int window, int window_demanding,
+                                              const float* similarity, int n_demanding,
+                                              uint8_t* expire_out) {
+  if (L < 1 || H < 1 || K < 1) return fail(HK_EINVAL, "L, H, K must be >= 1");
+  if (!scale_tokens || !expire_out) return fail(HK_EINVAL, "null argument");
+  for (int s = 0; s < K; ++s)
+    if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+  if (n_condensed < 0 || n_condensed > K) return fail(HK_EINVAL, "n_condensed must be in [0, K]");
+  if (window < 0 || window_demanding < 0) return fail(HK_EINVAL, "windows must be >= 0");
+  if (n_demanding < 0 || n_demanding > L) return fail(HK_EINVAL, "n_demanding must be in [0, L]");
+  if (n_demanding > 0 && !similarity)
+    return fail(HK_EINVAL, "n_demanding > 0 needs a similarity score per layer");
+  // Cache-demanding layers: the n_demanding lowest similarity scores, ties
+  // by the lower layer index.
+  std::vector<int> order(L);
+  std::iota(order.begin(), order.end(), 0);
+  std::vector<uint8_t> wide(L, 0);
+  if (n_demanding > 0) {
+    std::sort(order.begin(), order.end(), [&](int a, int b) {
+      return similarity[a] < similarity[b] || (similarity[a] == similarity[b] && a < b);
+    });
+    for (int i = 0; i < n_demanding; ++i) wide[order[i]] = 1;
+  }
+  for (int l = 0; l < L; ++l) {
+    const int64_t w = wide[l] ? window_demanding : window;
+    for (int h = 0; h < H; ++h)
+      for (int s = 0; s < K; ++s)
+        expire_out[(int64_t(l) * H + h) * K + s] =
+            uint8_t(s < n_condensed ? K - 1 : std::min<int64_t>(s + w, K - 1));
+  }
+  return HK_OK;
+}

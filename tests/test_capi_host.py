@@ -8,6 +8,7 @@ import pytest
 
 import workloads
 from oracle import cache as ocache
+from oracle import policies as opol
 from oracle import progressive as opr
 from oracle import schedule as osch
 
@@ -32,7 +33,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -222,3 +223,19 @@ def test_expiry_errors():
     with pytest.raises(hk.HeatKVError) as e:
         hk.build_progressive_schedule(t, (1, 4, 9, 16), 0.01, 1)
     assert e.value.status == hk.HK_EBUDGET
+
+
+def test_scale_window_schedule_matches_oracle():
+    g = np.random.default_rng(3)
+    for i in range(300):
+        L, H, K = int(g.integers(1, 6)), int(g.integers(1, 4)), int(g.integers(1, 14))
+        tokens = workloads.random_tokens(K, 900 + i, max_side=6)
+        c, w, wd = int(g.integers(0, K + 1)), int(g.integers(0, K + 2)), int(g.integers(0, K + 2))
+        nd = int(g.integers(0, L + 1))
+        sim = np.round(g.random(L) * 3).astype(np.float32)  # ties
+        got = hk.build_scale_window_schedule(L, H, tokens, c, w, wd, sim, nd)
+        want = opol.scale_window_schedule(L, H, tokens, c, w, wd, sim, nd)
+        np.testing.assert_array_equal(got, want)
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.build_scale_window_schedule(2, 1, (1, 4), 1, 1, 1, None, 1)
+    assert e.value.status == hk.HK_EINVAL

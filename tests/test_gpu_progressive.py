@@ -10,6 +10,7 @@ import torch
 
 import workloads
 from oracle import attention as oatt
+from oracle import policies as opol
 from oracle import progressive as opr
 from oracle.numerics import to_f64
 
@@ -249,4 +250,22 @@ def test_progressive_infinity2b_budget10_two_layers():
         hi = int(ctx.base[l, -1]) + wl.batch * int(ctx.cap[l, -1]) * wl.head_dim
         for c in (ctx.k_cache, ctx.v_cache):
             assert (to_host_bits(c[lo:hi]) == SENTINEL_BF16).all(), l
+    ctx.close()
+
+
+@pytest.mark.parametrize("mode", ["fused", "multi"])
+def test_scale_window_policy_bf16(mode):
+    """Condensed + local scale-window schedule: two condensed scales, a window
+    of two local scales, four in the least similar layer.  The oldest local
+    segment leaves from the middle of the cache at every step."""
+    wl = _wl(95, (1, 2, 3, 4, 6, 8, 12, 16, 20), layers=3, heads=2, head_dim=128, batch=2,
+             dtype="bf16")
+    sim = [0.5, 0.2, 0.9]
+    exp = hk.build_scale_window_schedule(3, 2, wl.scale_tokens, 2, 2, 4, sim, 1)
+    np.testing.assert_array_equal(exp, opol.scale_window_schedule(3, 2, wl.scale_tokens, 2, 2, 4,
+                                                                  sim, 1))
+    ctx, inputs, outs, table = _drive(wl, exp, mode, scas=(mode == "fused"))
+    _check_outputs(wl, exp, inputs, outs, [0, 1, 2])
+    if table is not None:
+        _check_scas(wl, exp, inputs, table, [0, 1, 2])
     ctx.close()

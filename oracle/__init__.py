@@ -27,8 +27,10 @@ Modules:
              after every layer, expiry steps and the cache contents they imply
   policies   condensed + local scale-window schedule (a second generator of
              expiry steps)
+  quant      (scale-block, channel) group-wise 4-bit storage of the cache and
+             attention over the dequantized segments
 
 Every function is written for readability, not speed.  Where the pages leave
 a step open, the reading taken is stated in the function's docstring.
 """
-from . import numerics, attention, schedule, cache, calibration, progressive, policies  # noqa: F401
+from . import numerics, attention, schedule, cache, calibration, progressive, policies, quant  # noqa: F401

@@ -214,6 +214,44 @@ int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
                      const int32_t* scale_tokens, const uint8_t* expire, int dtype,
                      void* k_cache, void* v_cache);
 
+/* 4-bit storage of the retained cache (VAR-Q summary page, Key
+ * contributions and Method: quantization groups indexed by (block, channel),
+ * a block being one scale's segment, optionally cut into sub-blocks along
+ * the token axis; low-bit values packed into bytes when written and unpacked
+ * for attention).  Readings taken:
+ *   sub-block j of a stored n-token segment is rows [j*n/m, (j+1)*n/m)
+ *     (rounded down), m = sub_blocks (the page's ratio r = 1/m);
+ *   per (sub-block, channel) group, in float32: lo = min, step = (max - lo)
+ *     / 15, code = round-half-even((x - lo) / step) clamped to [0, 15], 0 when
+ *     step = 0; an empty sub-block stores (0, 0); the value read back is
+ *     lo + code * step, rounded to bf16;
+ *   two codes per byte, even channel in the low nibble.
+ * Only the segments the static keep-mask keeps are stored (pruning and
+ * quantization compose).  Buffer layout (one buffer for K, one for V, bytes):
+ *   codes of head (l, h) from code_base(l, h) = sum over earlier heads of
+ *     B * cap * 64, as [B][cap][64];
+ *   from param_offset (256-byte aligned) the groups of head (l, h), as
+ *     [B][m * stored segments][128] float2 (step, lo), segments in scale
+ *     order.
+ * Supported: bf16 inputs with D = 128.
+ *   store_bytes_out   host int64 (required): bytes of each buffer
+ *   param_offset_out  host int64 or NULL
+ * Errors: HK_EINVAL, HK_EUNSUPPORTED. */
+int hk_layout_int4(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* keep, int B,
+                   int D, int sub_blocks, int64_t* store_bytes_out, int64_t* param_offset_out);
+
+/* Create a context whose cache is stored in 4 bits (hk_layout_int4) in the
+ * caller's k_store / v_store.  Queries, current keys and values and outputs
+ * stay bf16 [B][n_t][H][128].  hk_append_scale (and the append half of
+ * hk_attend_append) quantizes the scale's stored segments into the buffers;
+ * hk_attend / hk_attend_with_scas first unpack the layer's held rows into a
+ * bf16 scratch the context owns (the largest layer's bf16 cache, allocated
+ * here) and then run the bf16 attention on it, so the matrix-core kernel
+ * does no per-query-tile unpacking.  Order rules as hk_create.
+ * Errors: as hk_create (HK_EUNSUPPORTED unless D = 128). */
+int hk_create_int4(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
+                   const uint8_t* keep, int sub_blocks, void* k_store, void* v_store);
+
 /* Free the context's device tables (synchronises the device first). NULL is OK. */
 int hk_destroy(hk_ctx* ctx);
 

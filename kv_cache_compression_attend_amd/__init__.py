@@ -79,6 +79,8 @@ def _load():
         "hk_layout_expiry": ([I, I, I, P, P, I, I, P, P, P], I),
         "hk_create_expiry": ([P, I, I, I, I, I, P, P, I, P, P], I),
         "hk_build_scale_window_schedule": ([I, I, I, P, I, I, I, P, I, P], I),
+        "hk_layout_int4": ([I, I, I, P, P, I, I, I, P, P], I),
+        "hk_create_int4": ([P, I, I, I, I, I, P, P, I, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -205,6 +207,21 @@ def layout_expiry(scale_tokens: Sequence[int], expire: np.ndarray, batch: int,
     return int(elems[0]), cap, base
 
 
+def layout_int4(scale_tokens: Sequence[int], keep: np.ndarray, batch: int, head_dim: int,
+                sub_blocks: int) -> Tuple[int, int]:
+    """(bytes of each 4-bit store buffer, byte offset of its group parameters)."""
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    L, H, K = keep.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    nbytes = np.zeros(1, dtype=np.int64)
+    poff = np.zeros(1, dtype=np.int64)
+    _check(_lib.hk_layout_int4(L, H, K, _ptr(tok), _ptr(keep), int(batch), int(head_dim),
+                               int(sub_blocks), _ptr(nbytes), _ptr(poff)))
+    return int(nbytes[0]), int(poff[0])
+
+
 def scas_mean(scas_sum: np.ndarray, images: float) -> np.ndarray:
     """S-CAS table [L][H][K][K] float32 from a streamed double sum and the image count."""
     scas_sum = np.ascontiguousarray(scas_sum, dtype=np.float64)
@@ -245,14 +262,23 @@ class Context:
     device unless ``k_cache``/``v_cache`` are given, and keeps them alive for
     the context's lifetime.  The schedule is a static keep-mask ``keep``
     [L][H][K], or expiry steps ``expire`` [L][H][K] (pass ``keep=None``).
+    With ``sub_blocks`` set (static keep-mask, bf16, head_dim 128) the cache
+    is stored in 4 bits: ``k_cache``/``v_cache`` are then uint8 buffers of
+    ``layout_int4`` bytes holding codes and group parameters.
     """
 
     def __init__(self, layers: int, heads: int, head_dim: int, batch: int,
                  scale_tokens: Sequence[int], keep: Optional[np.ndarray], dtype: torch.dtype,
                  k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
-                 device=None, expire: Optional[np.ndarray] = None):
+                 device=None, expire: Optional[np.ndarray] = None,
+                 sub_blocks: Optional[int] = None):
         if dtype not in DTYPES:
             raise HeatKVError(HK_EUNSUPPORTED, f"dtype {dtype} not supported")
+        self.sub_blocks = sub_blocks
+        if sub_blocks is not None:
+            self._init_int4(layers, heads, head_dim, batch, scale_tokens, keep, dtype, k_cache,
+                            v_cache, device, int(sub_blocks))
+            return
         self.L, self.H, self.D, self.B = int(layers), int(heads), int(head_dim), int(batch)
         self.tokens = tuple(int(x) for x in scale_tokens)
         self.K = len(self.tokens)
@@ -290,6 +316,41 @@ class Context:
                           _ptr(tok), _ptr(table), DTYPES[dtype],
                           ctypes.c_void_p(k_cache.data_ptr()),
                           ctypes.c_void_p(v_cache.data_ptr())))
+        self._h = handle
+
+    def _init_int4(self, layers, heads, head_dim, batch, scale_tokens, keep, dtype, k_store,
+                   v_store, device, m):
+        if dtype != torch.bfloat16 or keep is None:
+            raise HeatKVError(HK_EUNSUPPORTED, "4-bit storage takes bf16 tensors and a keep-mask")
+        self.L, self.H, self.D, self.B = int(layers), int(heads), int(head_dim), int(batch)
+        self.tokens = tuple(int(x) for x in scale_tokens)
+        self.K = len(self.tokens)
+        self.dtype = dtype
+        self.expire = None
+        self.keep = np.ascontiguousarray(keep, dtype=np.uint8)
+        if self.keep.shape != (self.L, self.H, self.K):
+            raise HeatKVError(HK_EINVAL, "keep must be [L][H][K]")
+        self.store_bytes, self.param_offset = layout_int4(self.tokens, self.keep, self.B, self.D, m)
+        _, self.cap, _ = layout(self.tokens, self.keep, self.B, self.D)
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        n_alloc = max(self.store_bytes, 16)
+        if k_store is None:
+            k_store = torch.empty(n_alloc, dtype=torch.uint8, device=dev)
+        if v_store is None:
+            v_store = torch.empty(n_alloc, dtype=torch.uint8, device=dev)
+        for c in (k_store, v_store):
+            if c.dtype != torch.uint8 or not c.is_cuda or not c.is_contiguous() or c.numel() < self.store_bytes:
+                raise HeatKVError(HK_EINVAL, "4-bit stores must be contiguous uint8 device tensors "
+                                             "of layout_int4() bytes")
+        self.k_cache, self.v_cache = k_store, v_store
+        self.device = k_store.device
+        tok = np.ascontiguousarray(self.tokens, dtype=np.int32)
+        handle = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(_lib.hk_create_int4(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
+                                       _ptr(tok), _ptr(self.keep), int(m),
+                                       ctypes.c_void_p(k_store.data_ptr()),
+                                       ctypes.c_void_p(v_store.data_ptr())))
         self._h = handle
 
     # -- argument checks (shapes the kernels and their grids assume) -------------------

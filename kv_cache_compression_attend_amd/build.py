@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libheatkv.so")
 
 HOST_SOURCES = ["schedule.cpp"]
 HIP_SOURCES = ["context.hip", "attend_bf16.hip", "attend_f32.hip", "scas_finalize.hip",
-               "compact.hip"]
+               "compact.hip", "quant.hip"]
 ARCH = "gfx950"
 
 

@@ -46,6 +46,17 @@ struct hk_ctx {
   float2* d_ws_ml = nullptr;      // split workspace: (max, denominator)
   std::vector<int> appended;      // last scale appended per layer (-1: none)
   std::vector<int> attended;      // last scale attended per layer (-1: none)
+  // 4-bit storage (quant_m > 0 sub-blocks per segment): kstore/vstore are the
+  // caller's code + parameter buffers; kcache/vcache then point at the
+  // context's bf16 scratch for one layer, which base[] indexes per layer.
+  int quant_m = 0;
+  void* kstore = nullptr;
+  void* vstore = nullptr;
+  std::vector<int64_t> qdesc_first;   // [K][L+1] quantize descriptors of (t, l)
+  std::vector<int64_t> uitem_first;   // [L] unpack items of layer l (sorted by scale)
+  std::vector<int64_t> uitem_count;   // [K][L] items attend(l, t) unpacks (a prefix)
+  hk::QuantDesc* d_qdesc = nullptr;
+  hk::UnpackItem* d_uitems = nullptr;
 };
 
 namespace {
@@ -79,6 +90,14 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_desc);
   (void)hipFree(c->d_gdesc);
   (void)hipFree(c->d_gruns);
+  (void)hipFree(c->d_qdesc);
+  (void)hipFree(c->d_uitems);
+  if (c->quant_m > 0) {
+    (void)hipFree(c->kcache);
+    (void)hipFree(c->vcache);
+    c->kcache = nullptr;
+    c->vcache = nullptr;
+  }
   (void)hipFree(c->d_partials);
   (void)hipFree(c->d_ws_o);
   (void)hipFree(c->d_ws_ml);
@@ -90,6 +109,8 @@ void free_tables(hk_ctx* c) {
   c->d_desc = nullptr;
   c->d_gdesc = nullptr;
   c->d_gruns = nullptr;
+  c->d_qdesc = nullptr;
+  c->d_uitems = nullptr;
   c->d_partials = nullptr;
 }
 
@@ -174,11 +195,27 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   // step (segment t is then stored where the attention still reads, after
   // the survivors); otherwise the gather and compaction kernels run after the
   // attention kernel.
-  const bool fused = append && c->dtype == HK_DTYPE_BF16 && !drops;
+  const bool fused = append && c->dtype == HK_DTYPE_BF16 && !drops && c->quant_m == 0;
   a.append = fused;
 
-  hipError_t e = c->dtype == HK_DTYPE_BF16 ? hk::launch_attend_bf16_d128(a, scas, s)
-                                           : hk::launch_attend_f32(a, c->D, scas, s);
+  hipError_t e = hipSuccess;
+  if (c->quant_m > 0) {
+    // 4-bit storage: unpack the layer's held rows into the bf16 scratch the
+    // attend kernel reads; the scale itself is quantized by the append.
+    a.append = 0;
+    hk::UnpackArgs u{};
+    u.items = c->d_uitems + c->uitem_first[layer];
+    u.n_items = int(c->uitem_count[int64_t(step) * c->L + layer]);
+    u.kstore = static_cast<const uint8_t*>(c->kstore);
+    u.vstore = static_cast<const uint8_t*>(c->vstore);
+    u.kscratch = static_cast<uint16_t*>(c->kcache);
+    u.vscratch = static_cast<uint16_t*>(c->vcache);
+    u.B = c->B;
+    e = hk::launch_unpack(u, s);
+    if (e != hipSuccess) return hip_fail(e, "unpack launch");
+  }
+  e = c->dtype == HK_DTYPE_BF16 ? hk::launch_attend_bf16_d128(a, scas, s)
+                                : hk::launch_attend_f32(a, c->D, scas, s);
   if (e != hipSuccess) return hip_fail(e, "attend launch");
   c->attended[layer] = step;
   if (scas) {
@@ -201,9 +238,12 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
 
 }  // namespace
 
-extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
-                                const int32_t* scale_tokens, const uint8_t* expire, int dtype,
-                                void* k_cache, void* v_cache) {
+namespace {
+
+// Builds a context for an expiry-step schedule.  quant_m > 0: 4-bit storage
+// in k_cache / v_cache (a static schedule, bf16 head_dim 128).
+int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
+                const uint8_t* expire, int dtype, void* k_cache, void* v_cache, int quant_m) {
   if (!out) return fail(HK_EINVAL, "null output pointer");
   *out = nullptr;
   if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
@@ -236,20 +276,39 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
 
   hk::step_tables(expire, scale_tokens, heads, K, c->lenb, c->cap);
   c->base.assign(heads, 0);
-  int64_t offset = 0;
+  int64_t offset = 0, scratch_elems = 0;
   for (int64_t f = 0; f < heads; ++f) {
     if (c->cap[f] > INT32_MAX) { delete c; return fail(HK_EINVAL, "head cache exceeds 2^31 rows"); }
+    // 4-bit storage: base[] indexes the one-layer bf16 scratch, so it
+    // restarts with every layer.
+    if (quant_m > 0 && f % H == 0) offset = 0;
     c->base[f] = offset;
     offset += c->cap[f] * B * D;
+    scratch_elems = std::max(scratch_elems, offset);
   }
-  const int64_t cache_elems = offset;
-  if (cache_elems > 0 && (!k_cache || !v_cache)) {
+  const int64_t cache_bytes = quant_m > 0 ? 0 : offset * c->elem_bytes;
+  std::vector<int64_t> code_base, param_base;
+  std::vector<int32_t> gcap;
+  std::vector<uint8_t> keep(heads * K);
+  for (int64_t i = 0; i < heads * K; ++i) keep[i] = expire[i] == K - 1 && i % K <= K - 2;
+  const int64_t store_bytes =
+      quant_m > 0 ? hk::int4_layout(keep.data(), c->cap, heads, K, B, D, quant_m, code_base,
+                                    param_base, gcap)
+                  : cache_bytes;
+  if (store_bytes > 0 && (!k_cache || !v_cache)) {
     delete c;
     return fail(HK_EINVAL, "null cache buffer");
   }
   if (!aligned16(k_cache) || !aligned16(v_cache)) {
     delete c;
     return fail(HK_EINVAL, "cache buffers must be 16-byte aligned");
+  }
+  if (quant_m > 0) {
+    c->quant_m = quant_m;
+    c->kstore = k_cache;
+    c->vstore = v_cache;
+    c->kcache = nullptr;
+    c->vcache = nullptr;
   }
   auto lenb_at = [&](int t, int64_t f, int s) { return c->lenb[(int64_t(t) * heads + f) * K + s]; };
 
@@ -271,7 +330,7 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
     for (int l = 0; l < L; ++l) {
       c->desc_first[int64_t(t) * (L + 1) + l] = int64_t(desc.size());
       c->gdesc_first[int64_t(t) * (L + 1) + l] = int64_t(gdesc.size());
-      if (t > K - 2) continue;
+      if (t > K - 2 || quant_m > 0) continue;
       for (int h = 0; h < H; ++h) {
         const int64_t f = int64_t(l) * H + h;
         for (int sd = 0; sd < t; ++sd)
@@ -299,6 +358,69 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
     }
     c->desc_first[int64_t(t) * (L + 1) + L] = int64_t(desc.size());
     c->gdesc_first[int64_t(t) * (L + 1) + L] = int64_t(gdesc.size());
+  }
+
+  // 4-bit storage: one quantize descriptor per stored (t, l, h); unpack
+  // items per layer in scale order (chunks of at most kUnpackRows rows of
+  // one sub-block group), so attend(l, t) unpacks a prefix of layer l's list.
+  std::vector<hk::QuantDesc> qdesc;
+  std::vector<hk::UnpackItem> uitems;
+  c->qdesc_first.assign(int64_t(K) * (L + 1), 0);
+  c->uitem_first.assign(L + 1, 0);
+  c->uitem_count.assign(int64_t(K) * L, 0);
+  if (quant_m > 0) {
+    for (int t = 0; t < K; ++t) {
+      for (int l = 0; l < L; ++l) {
+        c->qdesc_first[int64_t(t) * (L + 1) + l] = int64_t(qdesc.size());
+        if (t > K - 2) continue;
+        for (int h = 0; h < H; ++h) {
+          const int64_t f = int64_t(l) * H + h;
+          if (!keep[f * K + t]) continue;
+          int before = 0;
+          for (int s2 = 0; s2 < t; ++s2) before += keep[f * K + s2];
+          hk::QuantDesc q{};
+          q.code_off = code_base[f] + int64_t(lenb_at(t + 1, f, t)) * hk::kQuantRowBytes;
+          q.param_off = param_base[f] + int64_t(quant_m) * before * D * int64_t(sizeof(float2));
+          q.cap = int32_t(c->cap[f]);
+          q.gcap = gcap[f];
+          q.head = h;
+          q.layer = l;
+          qdesc.push_back(q);
+        }
+      }
+      c->qdesc_first[int64_t(t) * (L + 1) + L] = int64_t(qdesc.size());
+    }
+    for (int l = 0; l < L; ++l) {
+      c->uitem_first[l] = int64_t(uitems.size());
+      for (int s2 = 0; s2 <= K - 2; ++s2) {
+        // Steps t > s2 read segment s2: every later step's prefix includes it.
+        for (int h = 0; h < H; ++h) {
+          const int64_t f = int64_t(l) * H + h;
+          if (!keep[f * K + s2]) continue;
+          int before = 0;
+          for (int s3 = 0; s3 < s2; ++s3) before += keep[f * K + s3];
+          const int n = scale_tokens[s2];
+          const int row0 = lenb_at(K - 1, f, s2);
+          for (int j = 0; j < quant_m; ++j) {
+            const int a = int(int64_t(j) * n / quant_m), b = int(int64_t(j + 1) * n / quant_m);
+            for (int r = a; r < b; r += hk::kUnpackRows) {
+              hk::UnpackItem u{};
+              u.code_off = code_base[f] + int64_t(row0 + r) * hk::kQuantRowBytes;
+              u.param_off = param_base[f] +
+                            (int64_t(quant_m) * before + j) * D * int64_t(sizeof(float2));
+              u.scratch_off = c->base[f] + int64_t(row0 + r) * D;
+              u.rows = std::min(hk::kUnpackRows, b - r);
+              u.cap = int32_t(c->cap[f]);
+              u.gcap = gcap[f];
+              uitems.push_back(u);
+            }
+          }
+        }
+        for (int t = s2 + 1; t < K; ++t)
+          c->uitem_count[int64_t(t) * L + l] = int64_t(uitems.size()) - c->uitem_first[l];
+      }
+    }
+    c->uitem_first[L] = int64_t(uitems.size());
   }
 
   int64_t max_partials = 1;
@@ -331,6 +453,13 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
   if (e == hipSuccess) e = upload(&c->d_desc, desc);
   if (e == hipSuccess) e = upload(&c->d_gdesc, gdesc);
   if (e == hipSuccess) e = upload(&c->d_gruns, gruns);
+  if (e == hipSuccess) e = upload(&c->d_qdesc, qdesc);
+  if (e == hipSuccess) e = upload(&c->d_uitems, uitems);
+  if (e == hipSuccess && quant_m > 0) {
+    const size_t bytes = size_t(std::max<int64_t>(scratch_elems, 1)) * sizeof(uint16_t);
+    e = hipMalloc(&c->kcache, bytes);
+    if (e == hipSuccess) e = hipMalloc(&c->vcache, bytes);
+  }
   if (e == hipSuccess)
     e = hipMalloc(reinterpret_cast<void**>(&c->d_partials),
                   size_t(max_partials) * hk::kMaxScales * sizeof(float));
@@ -345,6 +474,29 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
   }
   *out = c;
   return HK_OK;
+}
+
+}  // namespace
+
+extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
+                                const int32_t* scale_tokens, const uint8_t* expire, int dtype,
+                                void* k_cache, void* v_cache) {
+  return create_impl(out, L, H, D, B, K, scale_tokens, expire, dtype, k_cache, v_cache, 0);
+}
+
+extern "C" int hk_create_int4(hk_ctx** out, int L, int H, int D, int B, int K,
+                              const int32_t* scale_tokens, const uint8_t* keep, int sub_blocks,
+                              void* k_store, void* v_store) {
+  if (!out) return fail(HK_EINVAL, "null output pointer");
+  *out = nullptr;
+  if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
+  if (!scale_tokens || !keep) return fail(HK_EINVAL, "null scale_tokens or keep");
+  if (D != hk::kQuantD) return fail(HK_EUNSUPPORTED, "4-bit storage needs head_dim 128 (got %d)", D);
+  if (sub_blocks < 1 || sub_blocks > 64) return fail(HK_EINVAL, "sub_blocks must be in [1, 64]");
+  std::vector<uint8_t> expire;
+  hk::expire_from_keep(keep, int64_t(L) * H, K, expire);
+  return create_impl(out, L, H, D, B, K, scale_tokens, expire.data(), HK_DTYPE_BF16, k_store,
+                     v_store, sub_blocks);
 }
 
 extern "C" int hk_create(hk_ctx** out, int L, int H, int D, int B, int K,
@@ -441,6 +593,31 @@ namespace {
 int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const void* k_cur,
                   const void* v_cur, int64_t layer_stride_elems, void* hip_stream) {
   const int nl = layer_end - layer_begin;
+  if (c->quant_m > 0) {
+    const int64_t qfirst = c->qdesc_first[int64_t(step) * (c->L + 1) + layer_begin];
+    const int64_t qlast = c->qdesc_first[int64_t(step) * (c->L + 1) + layer_end];
+    if (qlast > qfirst) {
+      DeviceGuard g(c->device);
+      if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+      hk::QuantArgs q{};
+      q.desc = c->d_qdesc + qfirst;
+      q.kcur = static_cast<const uint16_t*>(k_cur);
+      q.vcur = static_cast<const uint16_t*>(v_cur);
+      q.kstore = static_cast<uint8_t*>(c->kstore);
+      q.vstore = static_cast<uint8_t*>(c->vstore);
+      q.layer_stride = nl > 1 ? layer_stride_elems : 0;
+      q.n_desc = int(qlast - qfirst);
+      q.m = c->quant_m;
+      q.B = c->B;
+      q.n = c->tokens[step];
+      q.H = c->H;
+      q.layer_begin = layer_begin;
+      hipError_t e = hk::launch_quantize(q, static_cast<hipStream_t>(hip_stream));
+      if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    }
+    for (int l = layer_begin; l < layer_end; ++l) c->appended[l] = step;
+    return HK_OK;
+  }
   const int64_t gfirst = c->gdesc_first[int64_t(step) * (c->L + 1) + layer_begin];
   const int64_t glast = c->gdesc_first[int64_t(step) * (c->L + 1) + layer_end];
   const int64_t first = c->desc_first[int64_t(step) * (c->L + 1) + layer_begin];

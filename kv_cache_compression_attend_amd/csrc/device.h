@@ -83,6 +83,55 @@ struct GatherArgs {
   int rows_per_chunk;     // rows moved per barrier interval
 };
 
+// 4-bit storage (head_dim 128): a row of 128 channels is 64 bytes of codes
+// (two per byte, even channel in the low nibble); every (sub-block, channel)
+// group has a float2 (step, lo).
+constexpr int kQuantD = 128;
+constexpr int kQuantRowBytes = kQuantD / 2;
+
+// Quantize one stored segment of a completed scale (one per (l, h) that
+// keeps scale t); the workgroup handles sub-block blockIdx.x % m.
+struct QuantDesc {
+  int64_t code_off;       // bytes: codes of (l, h, b=0), first row of the segment
+  int64_t param_off;      // bytes: params of (l, h, b=0), first group of the segment
+  int32_t cap;            // rows per batch entry of (l, h)
+  int32_t gcap;           // groups per batch entry of (l, h)
+  int32_t head;
+  int32_t layer;
+};
+
+struct QuantArgs {
+  const QuantDesc* desc;
+  const uint16_t* kcur;   // bf16 [layers][B][n][H][D]
+  const uint16_t* vcur;
+  uint8_t* kstore;
+  uint8_t* vstore;
+  int64_t layer_stride;   // elements between consecutive layers' tensors
+  int n_desc, m, B, n, H, layer_begin;
+};
+
+// Unpack a run of stored rows (one sub-block group, at most kUnpackRows
+// rows) of one head into the bf16 scratch that attend reads.
+struct UnpackItem {
+  int64_t code_off;       // bytes: codes of (l, h, b=0), first row of the run
+  int64_t param_off;      // bytes: params of (l, h, b=0), the run's group
+  int64_t scratch_off;    // elements: scratch of (h, b=0), first row of the run
+  int32_t rows;
+  int32_t cap;            // rows per batch entry (codes and scratch)
+  int32_t gcap;           // groups per batch entry
+  int32_t pad;
+};
+constexpr int kUnpackRows = 256;
+
+struct UnpackArgs {
+  const UnpackItem* items;
+  const uint8_t* kstore;
+  const uint8_t* vstore;
+  uint16_t* kscratch;     // bf16
+  uint16_t* vscratch;
+  int n_items, B;
+};
+
 // Workgroups are handed to the 8 dies round-robin (workgroup i runs on die
 // i % 8).  This maps the hardware index to a logical index so that each die
 // receives one contiguous range of logical work, keeping a head's query tiles
@@ -113,5 +162,7 @@ hipError_t launch_scas_accumulate(const float* partials, double* table, int laye
                                   int B, int n, int step, int n_qtiles, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
+hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);
 
 }  // namespace hk

@@ -95,4 +95,33 @@ inline void step_moves(const uint8_t* exp_f, const int32_t* tokens, int K, int t
   }
 }
 
+// 4-bit storage of a static keep-mask (one buffer each for K and V, bytes):
+// codes of head f at code_base[f], [B][cap[f]][D/2]; then, from
+// param_offset (256-byte aligned), the group parameters of head f at
+// param_base[f], [B][gcap[f]][D] float2 (step, lo), gcap[f] = m * (number of
+// stored segments), segment s's m groups following those of the stored
+// segments before it.
+inline int64_t int4_layout(const uint8_t* keep, const std::vector<int64_t>& cap, int64_t heads,
+                           int K, int B, int D, int m, std::vector<int64_t>& code_base,
+                           std::vector<int64_t>& param_base, std::vector<int32_t>& gcap) {
+  code_base.assign(heads, 0);
+  param_base.assign(heads, 0);
+  gcap.assign(heads, 0);
+  int64_t off = 0;
+  for (int64_t f = 0; f < heads; ++f) {
+    code_base[f] = off;
+    off += int64_t(B) * cap[f] * (D / 2);
+    int stored = 0;
+    for (int s = 0; s <= K - 2; ++s) stored += keep[f * K + s] ? 1 : 0;
+    gcap[f] = m * stored;
+  }
+  const int64_t param_offset = (off + 255) / 256 * 256;
+  off = param_offset;
+  for (int64_t f = 0; f < heads; ++f) {
+    param_base[f] = off;
+    off += int64_t(B) * gcap[f] * D * 8;
+  }
+  return off;
+}
+
 }  // namespace hk

@@ -207,6 +207,28 @@ extern "C" int hk_layout_expiry(int L, int H, int K, const int32_t* scale_tokens
   return HK_OK;
 }
 
+extern "C" int hk_layout_int4(int L, int H, int K, const int32_t* scale_tokens,
+                              const uint8_t* keep, int B, int D, int sub_blocks,
+                              int64_t* store_bytes_out, int64_t* param_offset_out) {
+  if (L < 1 || H < 1 || K < 1 || B < 1) return fail(HK_EINVAL, "sizes must be >= 1");
+  if (!scale_tokens || !keep || !store_bytes_out) return fail(HK_EINVAL, "null argument");
+  if (D != 128) return fail(HK_EUNSUPPORTED, "4-bit storage needs head_dim 128 (got %d)", D);
+  if (sub_blocks < 1 || sub_blocks > 64) return fail(HK_EINVAL, "sub_blocks must be in [1, 64]");
+  for (int s = 0; s < K; ++s)
+    if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+  const int64_t heads = int64_t(L) * H;
+  std::vector<uint8_t> expire, kept(heads * K);
+  hk::expire_from_keep(keep, heads, K, expire);
+  for (int64_t i = 0; i < heads * K; ++i) kept[i] = expire[i] == K - 1 && i % K <= K - 2;
+  std::vector<int32_t> lenb, gcap;
+  std::vector<int64_t> cap, code_base, param_base;
+  hk::step_tables(expire.data(), scale_tokens, heads, K, lenb, cap);
+  *store_bytes_out =
+      hk::int4_layout(kept.data(), cap, heads, K, B, D, sub_blocks, code_base, param_base, gcap);
+  if (param_offset_out) *param_offset_out = heads > 0 ? param_base[0] : 0;
+  return HK_OK;
+}
+
 extern "C" int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* keep,
                          int B, int D, int64_t* cache_elems_out, int64_t* cap_out,
                          int64_t* base_out) {

@@ -111,23 +111,36 @@ def stored_segments(x_scales: Sequence[np.ndarray], keep_lh: Sequence[int], k: i
     return out
 
 
-def attend_rows(q: np.ndarray, k_scales: Sequence[np.ndarray], v_scales: Sequence[np.ndarray],
-                keep_lh: Sequence[int], t: int, b: int, h: int, m: int, alpha: float,
-                rows=None) -> np.ndarray:
-    """Attention of query rows of scale t of (b, h) over the dequantized kept
-    segments s < t followed by scale t's own keys and values (fp64).
-    q: [B][n_t][H][D]; k_scales/v_scales[s]: [B][n_s][H][D] float32 values."""
-    kparts, vparts = [], []
+def dequantized_keys(k_scales: Sequence[np.ndarray], v_scales: Sequence[np.ndarray],
+                     keep_lh: Sequence[int], t: int, b: int, h: int, m: int):
+    """The keys and values a query of scale t of (b, h) reads: the dequantized
+    kept segments s < t, then scale t's own rows (fp64).  Returns (K_J, V_J,
+    sources, lengths) like ``attention.gather_keys``.
+    k_scales/v_scales[s]: [B][n_s][H][D] float32 values."""
+    kparts, vparts, src, lens = [], [], [], []
     for s in range(t):
         if s <= len(keep_lh) - 2 and keep_lh[s]:
             for xs, parts in ((k_scales, kparts), (v_scales, vparts)):
                 codes, step, lo = quantize_segment(xs[s][b, :, h, :], m)
                 parts.append(dequantize_segment(codes, step, lo, m))
+            src.append(s)
+            lens.append(k_scales[s].shape[1])
     kparts.append(np.asarray(k_scales[t][b, :, h, :], dtype=np.float64))
     vparts.append(np.asarray(v_scales[t][b, :, h, :], dtype=np.float64))
+    src.append(t)
+    lens.append(k_scales[t].shape[1])
+    return np.concatenate(kparts, axis=0), np.concatenate(vparts, axis=0), src, lens
+
+
+def attend_rows(q: np.ndarray, k_scales: Sequence[np.ndarray], v_scales: Sequence[np.ndarray],
+                keep_lh: Sequence[int], t: int, b: int, h: int, m: int, alpha: float,
+                rows=None) -> np.ndarray:
+    """Attention of query rows of scale t of (b, h) over the dequantized kept
+    segments s < t followed by scale t's own keys and values (fp64).
+    q: [B][n_t][H][D]."""
+    kj, vj, _, _ = dequantized_keys(k_scales, v_scales, keep_lh, t, b, h, m)
     qr = np.asarray(q[b, :, h, :], dtype=np.float64)
     if rows is not None:
         qr = qr[rows]
-    out, _ = softmax_attention(qr, np.concatenate(kparts, axis=0), np.concatenate(vparts, axis=0),
-                               alpha)
+    out, _ = softmax_attention(qr, kj, vj, alpha)
     return out

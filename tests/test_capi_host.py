@@ -28,12 +28,12 @@ import kv_cache_compression_attend_amd as hk  # noqa: E402
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(hk_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(hk_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 20, names
+    assert len(names) == 22, names
     lib = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(lib, n), n
@@ -238,4 +238,26 @@ def test_scale_window_schedule_matches_oracle():
         np.testing.assert_array_equal(got, want)
     with pytest.raises(hk.HeatKVError) as e:
         hk.build_scale_window_schedule(2, 1, (1, 4), 1, 1, 1, None, 1)
+    assert e.value.status == hk.HK_EINVAL
+
+
+def test_int4_layout_matches_its_definition():
+    for key in ("c0", "c2", "c4"):
+        wl = workloads.get(key)
+        keep = workloads.random_drop2_keep(wl) if wl.schedule == "random_drop2" else \
+            osch.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, wl.budget, wl.n_sink)[0]
+        for m in (1, 2, 8):
+            if wl.head_dim != 128:
+                with pytest.raises(hk.HeatKVError) as e:
+                    hk.layout_int4(wl.scale_tokens, keep, wl.batch, wl.head_dim, m)
+                assert e.value.status == hk.HK_EUNSUPPORTED
+                continue
+            nbytes, poff = hk.layout_int4(wl.scale_tokens, keep, wl.batch, wl.head_dim, m)
+            cap = ocache.capacity(keep, wl.scale_tokens)
+            code = int(cap.sum()) * wl.batch * 64
+            assert poff == (code + 255) // 256 * 256
+            stored = int(keep[:, :, : wl.n_scales - 1].sum())
+            assert nbytes == poff + stored * m * wl.batch * 128 * 8
+    with pytest.raises(hk.HeatKVError) as e:
+        hk.layout_int4((1, 4), np.ones((1, 1, 2), np.uint8), 1, 128, 0)
     assert e.value.status == hk.HK_EINVAL

@@ -263,6 +263,7 @@ def main():
         result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
         result["progressive_10pct"] = progressive_rate(args, hk, workloads, torch, np, dev, stream)
         result["scale_window"] = window_rate(args, hk, workloads, torch, np, dev, stream)
+        result["int4_10pct"] = int4_rate(args, hk, workloads, torch, np, dev, stream)
         result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
 
     # ---------------- calibration: S-CAS cost and ranking stability ----------------
@@ -369,7 +370,7 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
     K = wl.n_scales
     flops = pass_flops(wl, None, held_table(expire, wl.scale_tokens))
     static_flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
-    ms, elems = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3)
+    ms, cache_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3)
     row_bytes = wl.head_dim * 2
     gather_bytes = sum(moved_rows(expire, wl.scale_tokens, t) for t in range(K)) * wl.batch \
         * row_bytes * 2 * 2
@@ -386,17 +387,24 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
             "live_peak_token_slots": int(live.max()),
             "budget_token_slots": budget_slots,
             "live_peak_GB": round(int(live.max()) * slot_bytes / 1e9, 3),
-            "allocated_cache_GB": round(elems * 2 * 2 / 1e9, 3),
+            "allocated_cache_GB": round(cache_bytes / 1e9, 3),
             "static_allocated_cache_GB": round(hk.layout(wl.scale_tokens, keep, wl.batch,
                                                          wl.head_dim)[0] * 2 * 2 / 1e9, 3),
             "passes": args.pruned_steps}
 
 
-def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed):
+def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed, keep=None, sub_blocks=None):
     """Mean time of whole passes (every layer and scale, attend_append) under
-    an expiry schedule, on seeded GPU inputs of the workload's shapes."""
-    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, None,
-                     torch.bfloat16, expire=expire)
+    an expiry schedule (or a keep-mask with 4-bit storage), on seeded GPU
+    inputs of the workload's shapes.  Returns (ms, bytes of the K and V caches)."""
+    if sub_blocks is None:
+        ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, None,
+                         torch.bfloat16, expire=expire)
+        cache_bytes = ctx.cache_elems * 2 * 2
+    else:
+        ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
+                         torch.bfloat16, sub_blocks=sub_blocks)
+        cache_bytes = ctx.store_bytes * 2
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     K, L = wl.n_scales, wl.layers
@@ -425,9 +433,30 @@ def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.pruned_steps
-    elems = ctx.cache_elems
     ctx.close()
-    return ms, elems
+    return ms, cache_bytes
+
+
+def int4_rate(args, hk, workloads, torch, np, dev, stream):
+    """The 32-layer, batch-8, 10%-budget workload with its retained cache
+    stored in 4 bits (one group per (scale, channel)): pass rate and cache
+    bytes against the bf16 cache of the same schedule."""
+    wl = workloads.get("c2")
+    keep, _, _ = hk.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, wl.budget,
+                                   wl.n_sink)
+    K = wl.n_scales
+    out = {"workload": "infinity2b-l32-b8-budget10-int4: the 10%-budget schedule, retained "
+                       "segments stored as 4-bit codes per (scale sub-block, channel) group"}
+    bf16_bytes = hk.layout(wl.scale_tokens, keep, wl.batch, wl.head_dim)[0] * 2 * 2
+    for m in (1, 8):
+        ms, store = expiry_pass(args, hk, wl, None, torch, dev, stream, 6, keep=keep, sub_blocks=m)
+        out[f"sub_blocks_{m}"] = {"ms_per_pass": round(ms, 3),
+                                  "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
+                                  "cache_GB": round(store / 1e9, 3),
+                                  "cache_vs_bf16": round(store / bf16_bytes, 4)}
+    out["bf16_cache_GB"] = round(bf16_bytes / 1e9, 3)
+    out["passes"] = args.pruned_steps
+    return out
 
 
 def window_rate(args, hk, workloads, torch, np, dev, stream):
@@ -439,7 +468,7 @@ def window_rate(args, hk, workloads, torch, np, dev, stream):
     K, L = wl.n_scales, wl.layers
     sim = np.random.default_rng(5).random(L).astype(np.float32)
     expire = hk.build_scale_window_schedule(L, wl.heads, wl.scale_tokens, 2, 2, K, sim, 4)
-    ms, elems = expiry_pass(args, hk, wl, expire, torch, dev, stream, 4)
+    ms, cache_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 4)
     full = L * wl.heads * sum(wl.scale_tokens[: K - 1])
     peak = max(hk.cache_size_after_layer(wl.scale_tokens, expire, k, l)
                for k in range(K) for l in range(L))
@@ -450,7 +479,7 @@ def window_rate(args, hk, workloads, torch, np, dev, stream):
             "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
             "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
             "live_peak_fraction_of_full_cache": round(peak / full, 4),
-            "allocated_cache_GB": round(elems * 2 * 2 / 1e9, 3),
+            "allocated_cache_GB": round(cache_bytes / 1e9, 3),
             "passes": args.pruned_steps}
 
 

@@ -120,8 +120,8 @@ int hk_layout(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* k
  *
  * Follows the Figure 4 caption of the Pith page of arXiv 2605.14877: after
  * scale k the pruning set G_k is the union over scales i <= k of the prefix
- * of length N_k of the ordering O_i, and must be absent by the end of scale
- * k; and the signature of its Algorithm 2, CacheSizeAfterLayer(k, l, G_k,
+ * of length N_k of the ordering O_i, which is to be gone from the cache once
+ * scale k is done; and the signature of its Algorithm 2, CacheSizeAfterLayer(k, l, G_k,
  * G_{k-1}, ...), which tracks the cache size layer by layer inside a scale.
  * Readings taken:
  *   orderings, prunable scales, sinks and the budget floor(budget_frac * F)

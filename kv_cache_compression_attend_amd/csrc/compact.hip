@@ -63,8 +63,8 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
 
 // In-place gather of one (layer, head, batch entry) cache region: the
 // segments that outlive the step move down over the dropped ones (Pith page
-// of arXiv 2605.14877, Figure 4 caption: a growing pruning set must be absent
-// by the end of its scale, so segments leave from the middle of the cache).
+// of arXiv 2605.14877, Figure 4 caption: a pruning set that grows is to be gone
+// from the cache once its scale is done, so segments leave from the middle of the cache).
 //
 // Destination rows are rewritten in ascending chunks, one workgroup per
 // region.  Every destination row's source row lies at or above it, so within

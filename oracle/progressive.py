@@ -8,8 +8,8 @@ appendix A, Algorithm 2):
   * every source scale i has an ordering O_i of the heads, from least to most
     dependent on the tokens of scale i;
   * after scale k the pruning set G_k is the union, over the scales i <= k,
-    of the prefix of length N_k of O_i, and G_k must be absent from the cache
-    by the end of scale k;
+    of the prefix of length N_k of O_i, and G_k is to be gone from the cache
+    once scale k is done;
   * the cache size is tracked layer by layer inside a scale
     (CacheSizeAfterLayer(k, l, G_k, G_{k-1}, ...)); the listing's body is not
     on the pages.

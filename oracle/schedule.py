@@ -8,7 +8,7 @@ Test infrastructure only.  The algorithm, in the pages' terms:
   * For every source scale i there is an ordering O_i of the heads, from
     least to most dependent on the tokens of scale i.  After scale k the
     pruning set G_k is the union over i <= k of the prefix of length N_k of
-    O_i; G_k is what must be absent by the end of scale k (Pith page of
+    O_i; G_k is to be gone from the cache once scale k is done (Pith page of
     arXiv 2605.14877, Figure 4 caption, the binary variant of Algorithm 1
     with greedy early pruning).
   * The budget decides how many low-ranked head-scale pairs are removed,

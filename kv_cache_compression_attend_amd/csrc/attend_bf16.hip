@@ -297,6 +297,63 @@ __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, in
   }
 }
 
+// Per-lane S-CAS accumulators: sc[src] is this query's unnormalised mass on
+// source src, relative to the running max.  Most 32-key blocks lie inside
+// one source segment, so their mass goes to one open accumulator (acc, for
+// source cur, whose keys end at hi); only a block that crosses a segment
+// boundary walks the segment list (scas_add) and moves the open segment on,
+// at most once per source per workgroup.
+struct ScasAcc {
+  float sc[kMaxScales];
+  float acc;
+  int cur, hi;
+};
+
+__device__ __forceinline__ int seg_hi(const AttendArgs& a, const Head& hd, int src) {
+  return src < a.step ? hd.lenb[src + 1] : hd.Ltot;
+}
+
+// The open segment: the first source whose keys end after key k.
+__device__ __forceinline__ void scas_open(const AttendArgs& a, const Head& hd, ScasAcc& x, int k) {
+  int src = 0;
+  while (src < a.step && seg_hi(a, hd, src) <= k) ++src;
+  x.cur = src;
+  x.hi = seg_hi(a, hd, src);
+}
+
+__device__ __forceinline__ void scas_init(const AttendArgs& a, const Head& hd, ScasAcc& x) {
+#pragma unroll
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s] = 0.f;
+  x.acc = 0.f;
+  scas_open(a, hd, x, 0);
+}
+
+__device__ __forceinline__ void scas_flush(ScasAcc& x) {
+#pragma unroll
+  for (int s = 0; s < kMaxScales; ++s)
+    if (s == x.cur) x.sc[s] += x.acc;
+  x.acc = 0.f;
+}
+
+__device__ __forceinline__ void scas_rescale(ScasAcc& x, float corr) {
+#pragma unroll
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s] *= corr;
+  x.acc *= corr;
+}
+
+// Adds one 32-key block (keys kblk.., this lane's probabilities p summing to
+// psum); blocks are added in key order.
+__device__ __forceinline__ void scas_block(const AttendArgs& a, const Head& hd, int hf,
+                                           const f32x16& p, float psum, int kblk, ScasAcc& x) {
+  if (kblk + 32 <= x.hi) {
+    x.acc += psum;
+    return;
+  }
+  scas_flush(x);
+  scas_add(a, hd, hf, p, psum, kblk, x.sc);
+  scas_open(a, hd, x, kblk + 32);
+}
+
 // Sums each source's normalised mass over the workgroup's valid queries and
 // writes the workgroup's partial row.
 template <int WAVES>
@@ -347,9 +404,8 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   f32x16 oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
-  float sc[kMaxScales];
-#pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) sc[s] = 0.f;
+  ScasAcc sa;
+  if constexpr (SCAS) scas_init(a, hd, sa);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -432,8 +488,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= corr;
       if constexpr (SCAS) {
-#pragma unroll
-        for (int src = 0; src < kMaxScales; ++src) sc[src] *= corr;
+        scas_rescale(sa, corr);
       }
     }
 
@@ -457,7 +512,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 #pragma unroll
         for (int v = 0; v < 16; ++v) psum += s[kb][v];
         l_run += psum;
-        scas_add(a, hd, hf, s[kb], psum, k0 + 32 * kb, sc);
+        scas_block(a, hd, hf, s[kb], psum, k0 + 32 * kb, sa);
       }
     } else {
       float l0 = 0.f, l1 = 0.f;
@@ -501,7 +556,10 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   }
   const float inv = 1.f / l_tot;
   store_out(a, hd, qrow, hf, oacc, inv);
-  if constexpr (SCAS) scas_reduce<4>(a, hd, qrow, inv, sc, sRed);
+  if constexpr (SCAS) {
+    scas_flush(sa);
+    scas_reduce<4>(a, hd, qrow, inv, sa.sc, sRed);
+  }
 }
 
 // Merges the splits of one output row: with M the largest split max and
@@ -556,9 +614,8 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 #pragma unroll
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  float sc[kMaxScales];
-#pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) sc[s] = 0.f;
+  ScasAcc sa;
+  if constexpr (SCAS) scas_init(a, hd, sa);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -618,8 +675,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
           pprev[half].w[w] = pack_bf16x2(bf16_lo(x) * corr, bf16_hi(x) * corr);
         }
       if constexpr (SCAS) {
-#pragma unroll
-        for (int src = 0; src < kMaxScales; ++src) sc[src] *= corr;
+        scas_rescale(sa, corr);
       }
     }
   };
@@ -728,14 +784,14 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     front(s0, k0, p1, last_c);
     const float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
                           std::true_type{}, s0, p0);
-    if constexpr (SCAS) scas_add(a, hd, hf, s0, e0, k0, sc);
+    if constexpr (SCAS) scas_block(a, hd, hf, s0, e0, k0, sa);
     __syncthreads();
 
     // step b: unit (t, keys 32..63)
     front(s1, k0 + 32, p0, last_c);
     const float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
                           std::integral_constant<bool, !LAST>{}, s1, p1);
-    if constexpr (SCAS) scas_add(a, hd, hf, s1, e1, k0 + 32, sc);
+    if constexpr (SCAS) scas_block(a, hd, hf, s1, e1, k0 + 32, sa);
     bk = bn;
   };
   using T_ = std::true_type;
@@ -751,7 +807,10 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 
   const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
   store_out(a, hd, qrow, hf, o, inv);
-  if constexpr (SCAS) scas_reduce<8>(a, hd, qrow, inv, sc, sRed);
+  if constexpr (SCAS) {
+    scas_flush(sa);
+    scas_reduce<8>(a, hd, qrow, inv, sa.sc, sRed);
+  }
 }
 
 }  // namespace

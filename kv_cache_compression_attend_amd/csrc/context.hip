@@ -57,6 +57,8 @@ struct hk_ctx {
   std::vector<int64_t> uitem_count;   // [K][L] items attend(l, t) unpacks (a prefix)
   hk::QuantDesc* d_qdesc = nullptr;
   hk::UnpackItem* d_uitems = nullptr;
+  float2* d_qminmax = nullptr;        // split-quantizer workspace
+  int64_t qminmax_slots = 0;          // its capacity in (desc, sub-block, chunk, b) slots
 };
 
 namespace {
@@ -92,6 +94,8 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_gruns);
   (void)hipFree(c->d_qdesc);
   (void)hipFree(c->d_uitems);
+  (void)hipFree(c->d_qminmax);
+  c->d_qminmax = nullptr;
   if (c->quant_m > 0) {
     (void)hipFree(c->kcache);
     (void)hipFree(c->vcache);
@@ -126,6 +130,12 @@ hipError_t upload(T** dst, const std::vector<T>& src) {
   if (e != hipSuccess) return e;
   if (src.empty()) return hipSuccess;
   return hipMemcpy(*dst, src.data(), src.size() * sizeof(T), hipMemcpyHostToDevice);
+}
+
+// Chunks of kQuantChunkRows rows covering the largest of m sub-blocks of n rows.
+int quant_chunks(int n, int m) {
+  const int rows = (n + m - 1) / m;
+  return std::max(1, (rows + hk::kQuantChunkRows - 1) / hk::kQuantChunkRows);
 }
 
 int check_step_args(const hk_ctx* c, int layer, int step) {
@@ -421,6 +431,11 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
       }
     }
     c->uitem_first[L] = int64_t(uitems.size());
+    for (int t = 0; t <= K - 2; ++t) {
+      const int64_t nd = c->qdesc_first[int64_t(t) * (L + 1) + L] - c->qdesc_first[int64_t(t) * (L + 1)];
+      c->qminmax_slots = std::max<int64_t>(
+          c->qminmax_slots, nd * quant_m * quant_chunks(scale_tokens[t], quant_m) * B);
+    }
   }
 
   int64_t max_partials = 1;
@@ -455,6 +470,9 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
   if (e == hipSuccess) e = upload(&c->d_gruns, gruns);
   if (e == hipSuccess) e = upload(&c->d_qdesc, qdesc);
   if (e == hipSuccess) e = upload(&c->d_uitems, uitems);
+  if (e == hipSuccess && c->qminmax_slots > 0)
+    e = hipMalloc(reinterpret_cast<void**>(&c->d_qminmax),
+                  size_t(c->qminmax_slots) * 2 * hk::kQuantD * sizeof(float2));
   if (e == hipSuccess && quant_m > 0) {
     const size_t bytes = size_t(std::max<int64_t>(scratch_elems, 1)) * sizeof(uint16_t);
     e = hipMalloc(&c->kcache, bytes);
@@ -612,6 +630,11 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
       q.n = c->tokens[step];
       q.H = c->H;
       q.layer_begin = layer_begin;
+      // Cut long sub-blocks into chunks when one workgroup per sub-block
+      // would leave most of the chip idle.
+      const int64_t single = int64_t(q.n_desc) * q.m * q.B * 2;
+      q.nch = single >= 2048 ? 1 : quant_chunks(q.n, q.m);
+      q.minmax = c->d_qminmax;
       hipError_t e = hk::launch_quantize(q, static_cast<hipStream_t>(hip_stream));
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
     }

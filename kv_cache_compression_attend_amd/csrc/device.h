@@ -108,7 +108,14 @@ struct QuantArgs {
   uint8_t* vstore;
   int64_t layer_stride;   // elements between consecutive layers' tensors
   int n_desc, m, B, n, H, layer_begin;
+  // Split form (nch > 1): each sub-block's rows are cut into nch chunks of
+  // kQuantChunkRows; a first launch writes per-chunk (min, max) pairs to
+  // minmax [n_desc][m][nch][B][2][D] (float2), a second one combines them
+  // and writes the codes.
+  int nch;
+  float2* minmax;
 };
+constexpr int kQuantChunkRows = 256;
 
 // Unpack a run of stored rows (one sub-block group, at most kUnpackRows
 // rows) of one head into the bf16 scratch that attend reads.

@@ -173,10 +173,138 @@ __global__ __launch_bounds__(kThreads) void unpack_kernel(UnpackArgs a) {
   }
 }
 
+// Split form, first launch.  grid: (n_desc * m * nch, B, 2): per-channel
+// (min, max) of one chunk of a sub-block's rows ((+inf, -inf) when empty).
+__global__ __launch_bounds__(kThreads) void quantize_minmax_kernel(QuantArgs a) {
+  __shared__ float sLo[16][kQuantD];
+  __shared__ float sHi[16][kQuantD];
+  const int ch = blockIdx.x % a.nch;
+  const int j = (blockIdx.x / a.nch) % a.m;
+  const int di = blockIdx.x / (a.nch * a.m);
+  const QuantDesc d = a.desc[di];
+  const int b = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  const int64_t tok = int64_t(a.H) * kQuantD;
+  const uint16_t* src = (is_v ? a.vcur : a.kcur) + int64_t(d.layer - a.layer_begin) * a.layer_stride +
+                        int64_t(b) * a.n * tok + int64_t(d.head) * kQuantD;
+  const int g0 = (j * a.n) / a.m, g1 = ((j + 1) * a.n) / a.m;
+  const int r0 = g0 + ch * kQuantChunkRows, r1 = min(g1, r0 + kQuantChunkRows);
+  const int i = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
+  float lo[8], hi[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lo[e] = INFINITY;
+    hi[e] = -INFINITY;
+  }
+  for (int r = r0 + i; r < r1; r += 16) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(src + r * tok + c8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x0 = bf16_lo(w[e]), x1 = bf16_hi(w[e]);
+      lo[2 * e] = fminf(lo[2 * e], x0);
+      hi[2 * e] = fmaxf(hi[2 * e], x0);
+      lo[2 * e + 1] = fminf(lo[2 * e + 1], x1);
+      hi[2 * e + 1] = fmaxf(hi[2 * e + 1], x1);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sLo[i][c8 + e] = lo[e];
+    sHi[i][c8 + e] = hi[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < kQuantD) {
+    const int c = threadIdx.x;
+    float l = INFINITY, h = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      l = fminf(l, sLo[k][c]);
+      h = fmaxf(h, sHi[k][c]);
+    }
+    const int64_t slot = ((int64_t(di) * a.m + j) * a.nch + ch) * a.B + b;
+    a.minmax[(slot * 2 + (is_v ? 1 : 0)) * kQuantD + c] = make_float2(l, h);
+  }
+}
+
+// Split form, second launch.  Same grid: the group's (min, max) from its
+// chunks (min and max are exact, so the order does not matter), the group
+// parameters (chunk 0 writes them), then this chunk's codes.
+__global__ __launch_bounds__(kThreads) void quantize_codes_kernel(QuantArgs a) {
+  __shared__ float sStep[kQuantD];
+  __shared__ float sBase[kQuantD];
+  const int ch = blockIdx.x % a.nch;
+  const int j = (blockIdx.x / a.nch) % a.m;
+  const int di = blockIdx.x / (a.nch * a.m);
+  const QuantDesc d = a.desc[di];
+  const int b = blockIdx.y;
+  const bool is_v = blockIdx.z == 1;
+  const int64_t tok = int64_t(a.H) * kQuantD;
+  const uint16_t* src = (is_v ? a.vcur : a.kcur) + int64_t(d.layer - a.layer_begin) * a.layer_stride +
+                        int64_t(b) * a.n * tok + int64_t(d.head) * kQuantD;
+  uint8_t* store = is_v ? a.vstore : a.kstore;
+  uint8_t* codes = store + d.code_off + int64_t(b) * d.cap * kQuantRowBytes;
+  const int g0 = (j * a.n) / a.m, g1 = ((j + 1) * a.n) / a.m;
+  if (threadIdx.x < kQuantD) {
+    const int c = threadIdx.x;
+    float lo = INFINITY, hi = -INFINITY;
+    for (int k = 0; k < a.nch; ++k) {
+      const int64_t slot = ((int64_t(di) * a.m + j) * a.nch + k) * a.B + b;
+      const float2 v = a.minmax[(slot * 2 + (is_v ? 1 : 0)) * kQuantD + c];
+      lo = fminf(lo, v.x);
+      hi = fmaxf(hi, v.y);
+    }
+    float step = 0.f, base = 0.f;
+    if (g1 > g0) {
+      base = lo;
+      step = (hi - lo) / 15.f;
+    }
+    sStep[c] = step;
+    sBase[c] = base;
+    if (ch == 0) {
+      float2* params = reinterpret_cast<float2*>(store + d.param_off +
+                                                 int64_t(b) * d.gcap * kQuantD * int64_t(sizeof(float2))) +
+                       j * kQuantD;
+      params[c] = make_float2(step, base);
+    }
+  }
+  __syncthreads();
+  const int r0 = g0 + ch * kQuantChunkRows, r1 = min(g1, r0 + kQuantChunkRows);
+  const int i = threadIdx.x >> 2, c32 = (threadIdx.x & 3) * 32;
+  float step[32], base[32];
+#pragma unroll
+  for (int e = 0; e < 32; ++e) {
+    step[e] = sStep[c32 + e];
+    base[e] = sBase[c32 + e];
+  }
+  for (int r = r0 + i; r < r1; r += 64) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(src + r * tok + c32);
+    u32x4 w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = p[k];
+    u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const unsigned word = w[e / 8][(e % 8) / 2];
+      const float x = (e % 2) ? bf16_hi(word) : bf16_lo(word);
+      out[e / 8] |= code_of(x, step[e], base[e]) << (4 * (e % 8));
+    }
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x4*>(codes + int64_t(r) * kQuantRowBytes +
+                                                               (threadIdx.x & 3) * 16));
+  }
+}
+
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n_desc == 0) return hipSuccess;
-  hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(a.n_desc * a.m), unsigned(a.B), 2u),
-                     dim3(kThreads), 0, s, a);
+  if (a.nch <= 1) {
+    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(a.n_desc * a.m), unsigned(a.B), 2u),
+                       dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  const dim3 grid(unsigned(a.n_desc * a.m * a.nch), unsigned(a.B), 2u);
+  hipLaunchKernelGGL(quantize_minmax_kernel, grid, dim3(kThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(quantize_codes_kernel, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

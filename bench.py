@@ -61,7 +61,62 @@ def parse():
                     help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                              "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM traffic profile of the final-scale attend launch from "
+                         "rocprofv3 counter CSVs of this benchmark and of --copy-probe, then exit")
     return ap.parse_args()
+
+
+def summarize_counters(paths):
+    """Traffic profile (bytes per launch) of the final-scale attend launch of
+    the default workload: FETCH_SIZE and WRITE_SIZE averaged over its
+    dispatches and scaled by what the same counters read for the 1 GiB
+    copies of --copy-probe."""
+    import csv
+
+    def per_dispatch(path, match):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if match(r["Kernel_Name"]):
+                    vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"no matching dispatch in {path}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    def is_kernel(name):
+        return "attend_q256_kernel<false>" in name
+
+    def is_copy(name):
+        return "copyBuffer" in name
+
+    fetch, nf = per_dispatch(paths[0], is_kernel)
+    write, nw = per_dispatch(paths[1], is_kernel)
+    copy_fetch, _ = per_dispatch(paths[2], is_copy)
+    copy_write, _ = per_dispatch(paths[3], is_copy)
+    gib_kib = float(1 << 20)
+    fs, ws = gib_kib / copy_fetch, gib_kib / copy_write
+    # Compulsory bytes of the launch: Q, cached K and V, current K and V, out.
+    B, H, D, n, cached = 1, 16, 128, 4096, 6425
+    algo = (4 * n + 2 * cached) * B * H * D * 2
+    total = (fetch * fs + write * ws) * 1024
+    return {"kernel": ROOFLINE_KERNEL,
+            "workload": "infinity2b-layer-full-b1, final scale (4,096 queries x 10,521 keys x 16 heads), one launch",
+            "kernel_sha256": attend_sources_sha(), "kernel_sources": ATTEND_SOURCES,
+            "fetch_size_kib_per_launch_raw": round(fetch, 2), "write_size_kib_per_launch_raw": round(write, 2),
+            "dispatches": [nf, nw], "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "scale_source": "1 GiB device-to-device copies of bench.py --copy-probe: FETCH_SIZE "
+                            f"{copy_fetch:,.1f} KiB, WRITE_SIZE {copy_write:,.1f} KiB per copy",
+            "bytes_per_launch": int(round(total)), "algorithmic_bytes_per_launch": algo,
+            "ratio_to_algorithmic": round(total / algo, 4),
+            "commands": [
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o run -- python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-pruned",
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o run -- python3 <repo>/bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-pruned",
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <cf> -o run -- python3 <repo>/bench.py --copy-probe",
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <cw> -o run -- python3 <repo>/bench.py --copy-probe",
+                "python3 <repo>/bench.py --summarize-counters <f>/run_counter_collection.csv "
+                "<w>/run_counter_collection.csv <cf>/run_counter_collection.csv <cw>/run_counter_collection.csv"]}
 
 
 def pass_flops(wl, keep, lenb_fn):
@@ -97,6 +152,9 @@ def lenb_table(keep, tokens):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",

@@ -35,6 +35,7 @@ HK_OK, HK_EINVAL, HK_EBUDGET, HK_EORDER, HK_EHIP, HK_EUNSUPPORTED = 0, -1, -2, -
 STATUS_NAMES = {HK_EINVAL: "EINVAL", HK_EBUDGET: "EBUDGET", HK_EORDER: "EORDER",
                 HK_EHIP: "EHIP", HK_EUNSUPPORTED: "EUNSUPPORTED"}
 HK_DTYPE_F32, HK_DTYPE_BF16 = 0, 1
+HK_MAX_SCALES = 16
 DTYPES = {torch.float32: HK_DTYPE_F32, torch.bfloat16: HK_DTYPE_BF16}
 
 

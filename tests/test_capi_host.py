@@ -261,3 +261,34 @@ def test_int4_layout_matches_its_definition():
     with pytest.raises(hk.HeatKVError) as e:
         hk.layout_int4((1, 4), np.ones((1, 1, 2), np.uint8), 1, 128, 0)
     assert e.value.status == hk.HK_EINVAL
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """The boundary is a C ABI: the header compiles as C99 and a C program
+    links against the library and calls a host entry point."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    src = tmp_path / "probe.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "heatkv.h"
+int main(void) {
+  int32_t tok[3] = {1, 4, 9};
+  uint8_t keep[3] = {1, 1, 0};
+  int64_t elems = 0;
+  int rc = hk_layout(1, 1, 3, tok, keep, 2, 16, &elems, NULL, NULL);
+  printf("%d %lld\n", rc, (long long)elems);
+  rc = hk_layout(0, 1, 3, tok, keep, 2, 16, &elems, NULL, NULL);
+  printf("%d %s\n", rc, hk_last_error());
+  return 0;
+}
+''')
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), LIB, "-Wl,-rpath," + os.path.dirname(LIB)],
+                   check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    assert out[0] == "0 160"            # (1 + 4) rows x batch 2 x 16 dims
+    assert out[1].startswith(str(hk.HK_EINVAL) + " ")

@@ -266,6 +266,31 @@ def test_streaming_calibration_over_batches():
                         assert got[l, h, t, s] == 0.0
 
 
+def test_maximum_scale_count_with_scas():
+    """HK_MAX_SCALES = 16 scales (every S-CAS accumulator in use), random
+    pruning, fused attend_append with S-CAS; outputs, S-CAS and cache."""
+    wl = _custom(84, "max-scales", tuple(range(1, 17)), heads=2, head_dim=128, batch=1, dtype="bf16")
+    assert wl.n_scales == hk.HK_MAX_SCALES
+    keep = _random_keep(wl, 84, p=0.7)
+    run = generate(wl, keep, [0], scas=True, fused=True)
+    _compare_outputs(run, [0], rows_per_unit=48)
+    _compare_scas(run, 0)
+    check_cache(run, [0])
+    run.ctx.close()
+
+
+def test_one_head_batch_one():
+    wl = _custom(85, "one-head", (1, 2, 3, 5, 8, 13), heads=1, head_dim=128, batch=1, dtype="bf16")
+    keep = np.ones((1, 1, wl.n_scales), dtype=np.uint8)
+    keep[0, 0, -1] = 0
+    keep[0, 0, 2] = 0
+    run = generate(wl, keep, [0], scas=True)
+    _compare_outputs(run, [0])
+    _compare_scas(run, 0)
+    check_cache(run, [0])
+    run.ctx.close()
+
+
 def test_single_scale_workload():
     wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
     keep = np.zeros((1, 2, 1), dtype=np.uint8)

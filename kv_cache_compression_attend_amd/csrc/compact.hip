@@ -120,6 +120,55 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// grid: (n_layers * B * ceil(n / rows)).  Item i of a workgroup is the i-th
+// 16-byte vector of its token block, so the loads walk the source
+// contiguously; a vector of a head that does not store this scale is skipped.
+__global__ __launch_bounds__(kCopyThreads) void compact_rows_kernel(RowsArgs a) {
+  const int nblk = (a.n + a.rows - 1) / a.rows;
+  const int blk = blockIdx.x % nblk;
+  const int b = (blockIdx.x / nblk) % a.B;
+  const int l = blockIdx.x / (nblk * a.B);
+  const int cpr = a.row_bytes >> 4;
+  const int per_tok = a.H * cpr;
+  const int r0 = blk * a.rows;
+  const int items = min(a.rows, a.n - r0) * per_tok;
+  const int64_t src0 = int64_t(l) * a.layer_stride_bytes + (int64_t(b) * a.n + r0) * per_tok * 16;
+  const int64_t* dst = a.dst + int64_t(l) * a.H;
+  const int32_t* cap = a.cap + int64_t(l) * a.H;
+  for (int base = threadIdx.x; base < items; base += kCopyThreads * kCopyItems) {
+    u32x4 kv[kCopyItems], vv[kCopyItems];
+    int64_t off[kCopyItems];
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      const int it = base + u * kCopyThreads;
+      off[u] = -1;
+      if (it < items) {
+        const int r = it / per_tok, h = (it / cpr) % a.H, c = it % cpr;
+        const int64_t d = dst[h];
+        if (d >= 0) {
+          off[u] = d + (int64_t(b) * cap[h] + r0 + r) * a.row_bytes + c * 16;
+          kv[u] = *reinterpret_cast<const u32x4*>(a.kcur + src0 + int64_t(it) * 16);
+          vv[u] = *reinterpret_cast<const u32x4*>(a.vcur + src0 + int64_t(it) * 16);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyItems; ++u) {
+      if (off[u] >= 0) {
+        __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(a.kcache + off[u]));
+        __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(a.vcache + off[u]));
+      }
+    }
+  }
+}
+
+hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s) {
+  const int64_t blocks = int64_t(a.n_layers) * a.B * ((a.n + a.rows - 1) / a.rows);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
   if (blocks == 0) return hipSuccess;

@@ -40,6 +40,7 @@ struct hk_ctx {
   hk::CopyDesc* d_desc = nullptr;
   hk::GatherDesc* d_gdesc = nullptr;
   hk::GatherRun* d_gruns = nullptr;
+  int64_t* d_rowdst = nullptr;    // [K][L][H] byte offset where (l, h) stores scale t, or -1
   float* d_partials = nullptr;
   std::vector<int> splits;        // [K] key-range splits of each scale's attend launch
   float* d_ws_o = nullptr;        // split workspace: unnormalised outputs
@@ -92,6 +93,8 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_desc);
   (void)hipFree(c->d_gdesc);
   (void)hipFree(c->d_gruns);
+  (void)hipFree(c->d_rowdst);
+  c->d_rowdst = nullptr;
   (void)hipFree(c->d_qdesc);
   (void)hipFree(c->d_uitems);
   (void)hipFree(c->d_qminmax);
@@ -330,6 +333,7 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
   // Per step: the heads that store segment t (at its row once the segments
   // expiring at t are gone) and the heads whose held segments move.
   std::vector<hk::CopyDesc> desc;
+  std::vector<int64_t> rowdst(int64_t(K) * heads, -1);
   std::vector<hk::GatherDesc> gdesc;
   std::vector<hk::GatherRun> gruns;
   std::vector<hk::MoveRun> runs;
@@ -360,6 +364,7 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
         if (expire[f * K + t] <= t) continue;
         hk::CopyDesc d{};
         d.dst = (c->base[f] + int64_t(lenb_at(t + 1, f, t)) * D) * c->elem_bytes;
+        rowdst[int64_t(t) * heads + f] = d.dst;
         d.cap = int32_t(c->cap[f]);
         d.head = h;
         d.layer = l;
@@ -467,6 +472,7 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
   if (e == hipSuccess) e = upload(&c->d_lenb, c->lenb);
   if (e == hipSuccess) e = upload(&c->d_desc, desc);
   if (e == hipSuccess) e = upload(&c->d_gdesc, gdesc);
+  if (e == hipSuccess && quant_m == 0) e = upload(&c->d_rowdst, rowdst);
   if (e == hipSuccess) e = upload(&c->d_gruns, gruns);
   if (e == hipSuccess) e = upload(&c->d_qdesc, qdesc);
   if (e == hipSuccess) e = upload(&c->d_uitems, uitems);
@@ -661,7 +667,32 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     hipError_t e = hk::launch_gather(a, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
-  if (last > first) {
+  const int row_bytes = c->D * c->elem_bytes;
+  const int rows_per_block = 32768 / row_bytes;
+  if (last > first && 2 * (last - first) >= int64_t(nl) * c->H && c->tokens[step] < rows_per_block) {
+    // A short scale that most heads store: per-head workgroups would each
+    // move less than one 32 KB block, so copy whole token blocks instead
+    // (contiguous reads, every head's rows written from one workgroup).  On
+    // long scales the per-head copy is faster (one contiguous write stream).
+    DeviceGuard g(c->device);
+    if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+    hk::RowsArgs a{};
+    a.dst = c->d_rowdst + (int64_t(step) * c->L + layer_begin) * c->H;
+    a.cap = c->d_cap + int64_t(layer_begin) * c->H;
+    a.kcur = static_cast<const uint8_t*>(k_cur);
+    a.vcur = static_cast<const uint8_t*>(v_cur);
+    a.kcache = static_cast<uint8_t*>(c->kcache);
+    a.vcache = static_cast<uint8_t*>(c->vcache);
+    a.layer_stride_bytes = nl > 1 ? layer_stride_elems * c->elem_bytes : 0;
+    a.n_layers = nl;
+    a.B = c->B;
+    a.n = c->tokens[step];
+    a.H = c->H;
+    a.row_bytes = row_bytes;
+    a.rows = std::max(1, 32768 / (c->H * row_bytes));   // 32 KB per tensor per workgroup
+    hipError_t e = hk::launch_compact_rows(a, static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return hip_fail(e, "compact launch");
+  } else if (last > first) {
     DeviceGuard g(c->device);
     if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
     hk::CompactArgs a{};
@@ -677,7 +708,7 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.H = c->H;
     a.row_bytes = c->D * c->elem_bytes;
     // 2048 16-byte vectors per tensor per workgroup: 8 per lane.
-    a.rows_per_block = std::min(std::max(1, 32768 / a.row_bytes), a.n);
+    a.rows_per_block = std::min(std::max(1, rows_per_block), a.n);
     a.chunks = (a.n + a.rows_per_block - 1) / a.rows_per_block;
     a.layer_begin = layer_begin;
     hipError_t e = hk::launch_compact(a, static_cast<hipStream_t>(hip_stream));

@@ -55,6 +55,22 @@ struct CompactArgs {
   int chunks;             // row blocks per (desc, b)
 };
 
+// Token-block compaction: a workgroup copies `rows` consecutive tokens of one
+// (layer, batch entry) for every head at once, reading them contiguously
+// ([n][H][D] source) and writing each stored head's run to its cache rows.
+struct RowsArgs {
+  const int64_t* dst;     // [layers][H] byte offset of row len_before of (l, h, b=0); -1: not stored
+  const int32_t* cap;     // [layers][H] rows per batch entry
+  const uint8_t* kcur;
+  const uint8_t* vcur;
+  uint8_t* kcache;
+  uint8_t* vcache;
+  int64_t layer_stride_bytes;
+  int n_layers, B, n, H;
+  int row_bytes;          // a multiple of 16
+  int rows;               // tokens per workgroup
+};
+
 // One (layer, head) whose cache loses segments at a step: the held segments
 // that outlive the step move down over the dropped ones.  The moves are runs
 // (dst row, src row, rows) in ascending order with dst < src, covering
@@ -168,6 +184,7 @@ hipError_t launch_scas_finalize(const float* partials, float* table, int layer, 
 hipError_t launch_scas_accumulate(const float* partials, double* table, int layer, int H, int K,
                                   int B, int n, int step, int n_qtiles, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);

@@ -291,6 +291,52 @@ def test_one_head_batch_one():
     run.ctx.close()
 
 
+def test_graph_capture_replays_match_eager():
+    """A whole pass (attend_append of every scale, with key-range splits and
+    the fused append) captured into a HIP graph replays to the eager result,
+    replay after replay, with eager passes in between: the per-scale calls
+    allocate nothing and record no memset nodes."""
+    wl = _custom(86, "graph", (1, 2, 4, 6, 8, 12, 16, 20, 24), heads=4, head_dim=128, batch=1,
+                 dtype="bf16")
+    keep = _random_keep(wl, 86, p=0.8)
+    ctx = hk.Context(1, wl.heads, 128, 1, wl.scale_tokens, keep, torch.bfloat16)
+    assert any(ctx.attend_plan(t)[1] > 1 for t in range(wl.n_scales)), "no split launch covered"
+    xs = [workloads.step_inputs(wl, 0, t, 0) for t in range(wl.n_scales)]
+    dev = [tuple(to_device(a, wl) for a in (x.q, x.k, x.v)) for x in xs]
+    outs = [torch.empty_like(d[0]) for d in dev]
+
+    def one_pass():
+        ctx.reset()
+        for t, (q, k, v) in enumerate(dev):
+            ctx.attend_append(0, t, q, k, v, outs[t], wl.softmax_scale)
+
+    one_pass()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_pass()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one_pass()
+    torch.cuda.synchronize()
+    for rep in range(5):
+        for o in outs:
+            o.zero_()
+        note(f"graph replay {rep}")
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, (a_, b_) in enumerate(zip(outs, ref)):
+            assert torch.equal(a_, b_), (rep, t)
+        one_pass()
+        torch.cuda.synchronize()
+    del graph
+    ctx.close()
+
+
 def test_single_scale_workload():
     wl = _custom(40, "single-scale", (9,), heads=2, head_dim=128, batch=2, dtype="bf16")
     keep = np.zeros((1, 2, 1), dtype=np.uint8)

@@ -35,7 +35,7 @@ METRIC = ("attend TFLOP/s + % bf16 MFMA peak; compact GB/s; scales/sec per image
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 ATTEND_SOURCES = ["kv_cache_compression_attend_amd/csrc/attend_bf16.hip",
-                  "kv_cache_compression_attend_amd/csrc/device.h"]
+                  "kv_cache_compression_attend_amd/csrc/attend.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_q256_infinity2b_layer_traffic.json")
 ROOFLINE_KERNEL = "attend_q256_kernel<false>"
 

@@ -59,7 +59,7 @@
 
 #include <type_traits>
 
-#include "device.h"
+#include "attend.h"
 
 namespace hk {
 

@@ -5,32 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attend.h"
+
 namespace hk {
-
-constexpr int kMaxScales = 16;   // S-CAS accumulators per query row
-constexpr int kXcds = 8;         // MI355X: 8 accelerator dies, 32 CUs each
-
-// Arguments of one attend launch: one layer, one scale step.
-struct AttendArgs {
-  const void* q;          // [B][n][H][D]
-  const void* kcur;       // [B][n][H][D]
-  const void* vcur;       // [B][n][H][D]
-  void* out;              // [B][n][H][D]
-  const void* kcache;     // whole K cache buffer
-  const void* vcache;     // whole V cache buffer
-  const int64_t* base;    // [H] element offset of head (layer, h)
-  const int32_t* cap;     // [H] cache rows per batch entry of head (layer, h)
-  const int32_t* lenb;    // [H][K] rows cached before each scale
-  float* partials;        // S-CAS partial sums [B*H*n_qtiles][kMaxScales]
-  float* ws_o;            // split launches: unnormalised outputs [n_split][B][n][H][D] fp32
-  float2* ws_ml;          // split launches: (running max, denominator) [n_split][B][n][H]
-  int B, H, n, K, step, n_qtiles;
-  int n_split;            // key-range splits per query tile (1: no split)
-  int append;             // 1: q-tile-0 workgroups also write this scale's kept
-                          // K/V rows into the cache (fused append)
-  float scale;            // softmax scale alpha
-  float scale_log2;       // alpha * log2(e)
-};
 
 // One kept (layer, head) segment of a completed scale, to be copied into the cache.
 struct CopyDesc {
@@ -155,30 +132,7 @@ struct UnpackArgs {
   int n_items, B;
 };
 
-// Workgroups are handed to the 8 dies round-robin (workgroup i runs on die
-// i % 8).  This maps the hardware index to a logical index so that each die
-// receives one contiguous range of logical work, keeping a head's query tiles
-// (which read the same keys and values) on one die and its L2.
-__device__ __forceinline__ int xcd_logical(int i, int n) {
-  const int q = n / kXcds, r = n % kXcds;
-  const int x = i % kXcds, k = i / kXcds;
-  return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
-}
-
-// Query rows per workgroup the bf16 attend launch uses for a scale of n
-// tokens (128 or 256); the S-CAS partial rows follow the same tiling.
-int attend_bf16_rows_per_workgroup(int B, int H, int n);
-
-// Key-range splits for a bf16 attend launch without S-CAS: 1 when the
-// launch fills the chip, else enough splits to give the 256 CUs two
-// workgroups each, keeping at least 4 key tiles per split of the longest head.
-int attend_bf16_splits(int B, int H, int n, int max_keys);
-
-// Launchers (defined next to their kernels).  a.n_qtiles must follow
-// attend_bf16_rows_per_workgroup and a.n_split attend_bf16_splits (or 1)
-// for the bf16 launch; a split launch also merges the splits into a.out.
-hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s);
-hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
+// Launchers, defined next to their kernels; each returns the launch status.
 hipError_t launch_scas_finalize(const float* partials, float* table, int layer, int H, int K,
                                 int B, int n, int step, int n_qtiles, hipStream_t s);
 hipError_t launch_scas_accumulate(const float* partials, double* table, int layer, int H, int K,

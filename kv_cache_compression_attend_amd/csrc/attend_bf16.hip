@@ -31,7 +31,12 @@
 //     The running max is raised only when a block's max exceeds it by more
 //     than 2^8, so the output accumulators are rescaled on a few blocks
 //     rather than on every one; probabilities stay below 256, which bf16 and
-//     fp32 hold as precisely as values below 1.
+//     fp32 hold as precisely as values below 1.  The exponentials are taken
+//     first, against the running max; only when a lane's probabilities sum
+//     to more than 2^7 (which any probability above 2^8 forces) does the
+//     wave take the block's exact max and, if it must, rescale and take the
+//     exponentials again.  The common block thus spends nothing on its max
+//     or on the cross-lane exchange the max needs.
 //   * Without S-CAS the softmax denominator is summed from the same bf16
 //     probabilities the value product uses (v_dot2 against ones: half the
 //     adds).  With S-CAS it is summed in fp32 together with per-source
@@ -77,6 +82,7 @@ constexpr int KSTR = D + 8;   // K tile row stride (bf16 elements): 272 bytes
 constexpr int VSTR = BN + 8;  // V^T tile row stride (bf16 elements): 144 bytes
 constexpr int kRowBytes = D * 2;
 constexpr float kRescaleSlack = 8.f;  // log2 units
+constexpr float kSumTrigger = 128.f;   // 2^(kRescaleSlack - 1)
 constexpr unsigned kOutOfRange = 0x80000000u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
@@ -269,12 +275,42 @@ __device__ __forceinline__ void store_out(const AttendArgs& a, const Head& hd, i
     }
 }
 
+// This lane's 16 probabilities of one 32-key block, 2^(s * c2 - m), packed
+// to bf16 pairs as the B operand of the value product (p[0]: keys of the
+// first 16-key step, p[1]: the second).  Returns their sum: of the fp32
+// values with F32SUM, else of the bf16 values the value product uses.
+template <bool F32SUM>
+__device__ __forceinline__ float exp_pack(const f32x16& s, float c2, float m, Vec16 (&p)[2]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; v += 2) {
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(s[v], c2, -m));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(s[v + 1], c2, -m));
+    uint32_t& w = p[v >> 3].w[(v & 7) >> 1];
+    w = pack_bf16x2(e0, e1);
+    if constexpr (F32SUM) sum += e0 + e1;
+    else sum = add_bf16x2(w, sum);
+  }
+  return sum;
+}
+
+// The probability of score register v, recomputed exactly as exp_pack and
+// the pipelined step compute it.
+struct ProbOf {
+  const f32x16& s;
+  float c2, m;
+  __device__ __forceinline__ float operator()(int v) const {
+    return __builtin_amdgcn_exp2f(fmaf(s[v], c2, -m));
+  }
+};
+
 // Adds this lane's probabilities of keys [kblk, kblk + 32) to the
 // accumulator of every source segment they fall in.  Source src < step
 // covers cache rows [lenb[src], lenb[src+1]); the current scale covers
 // [Lc, Ltot).  Bounds are wave-uniform scalar loads.
+template <typename Prob>
 __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, int hf,
-                                         const f32x16& p, float psum, int kblk,
+                                         const Prob& prob, float psum, int kblk,
                                          float (&sc)[kMaxScales]) {
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
@@ -289,7 +325,7 @@ __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, in
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kblk + key_of(v, hf);
-          acc += (key >= lo && key < hi) ? p[v] : 0.f;
+          acc += (key >= lo && key < hi) ? prob(v) : 0.f;
         }
       }
       sc[src] += acc;
@@ -341,16 +377,17 @@ __device__ __forceinline__ void scas_rescale(ScasAcc& x, float corr) {
   x.acc *= corr;
 }
 
-// Adds one 32-key block (keys kblk.., this lane's probabilities p summing to
-// psum); blocks are added in key order.
+// Adds one 32-key block (keys kblk.., this lane's probabilities prob(v),
+// v = 0..15, summing to psum); blocks are added in key order.
+template <typename Prob>
 __device__ __forceinline__ void scas_block(const AttendArgs& a, const Head& hd, int hf,
-                                           const f32x16& p, float psum, int kblk, ScasAcc& x) {
+                                           const Prob& prob, float psum, int kblk, ScasAcc& x) {
   if (kblk + 32 <= x.hi) {
     x.acc += psum;
     return;
   }
   scas_flush(x);
-  scas_add(a, hd, hf, p, psum, kblk, x.sc);
+  scas_add(a, hd, hf, prob, psum, kblk, x.sc);
   scas_open(a, hd, x, kblk + 32);
 }
 
@@ -473,57 +510,37 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
           if (k0 + 32 * kb + key_of(v, hf) >= Ltot) s[kb][v] = -INFINITY;
     }
 
-    float tmax = -INFINITY;
+    // Exponentials against the running max, then the lazy-max check (the
+    // same rule as the 256-query kernel; no value product of this tile has
+    // been issued yet, so a rescale covers all of the accumulators).
+    Vec16 pb[2][2];
+    float ps[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) ps[kb] = exp_pack<SCAS>(s[kb], c2, m_run, pb[kb]);
+    if (__builtin_expect(__any(!(ps[0] + ps[1] <= kSumTrigger)), 0)) {
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[kb][v]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mt = tmax * c2;
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= corr;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= corr;
-      if constexpr (SCAS) {
-        scas_rescale(sa, corr);
+        for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, s[kb][v]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mt = tmax * c2;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= corr;
+        if constexpr (SCAS) scas_rescale(sa, corr);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) ps[kb] = exp_pack<SCAS>(s[kb], c2, m_run, pb[kb]);
       }
     }
-
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = __builtin_amdgcn_exp2f(fmaf(s[kb][v], c2, -m_run));
-
-    // Probabilities as the B operand of O^T += V^T P^T, 16 keys per step.
-    Vec16 pb[4];
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st >> 1, base = 8 * (st & 1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) pb[st].w[w] = pack_bf16x2(s[kb][base + 2 * w], s[kb][base + 2 * w + 1]);
-    }
+    l_run += ps[0] + ps[1];
     if constexpr (SCAS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float psum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) psum += s[kb][v];
-        l_run += psum;
-        scas_block(a, hd, hf, s[kb], psum, k0 + 32 * kb, sa);
-      }
-    } else {
-      float l0 = 0.f, l1 = 0.f;
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        l0 = add_bf16x2(pb[st].w[0], l0);
-        l1 = add_bf16x2(pb[st].w[1], l1);
-        l0 = add_bf16x2(pb[st].w[2], l0);
-        l1 = add_bf16x2(pb[st].w[3], l1);
-      }
-      l_run += l0 + l1;
+      for (int kb = 0; kb < 2; ++kb) scas_block(a, hd, hf, ProbOf{s[kb], c2, m_run}, ps[kb], k0 + 32 * kb, sa);
     }
 
 #pragma unroll
@@ -532,7 +549,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
       for (int db = 0; db < 4; ++db) {
         Vec16 vf;
         vf.u = *reinterpret_cast<const u32x4*>(&sV[buf][(32 * db + j) * VSTR + 16 * st + 8 * hf]);
-        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, pb[st].b, oacc[db], 0, 0, 0);
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, pb[st >> 1][st & 1].b, oacc[db], 0, 0, 0);
       }
     }
     __syncthreads();
@@ -644,40 +661,41 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       }
     }
   };
-  // Softmax front: tail mask (last tile only), block max, lazy rescale.  A
-  // rescale also scales the probabilities of the previous unit, whose value
-  // product is still to be issued, and the S-CAS sums, which already hold it.
-  auto front = [&](f32x16& s, int kblk, Vec16 (&pprev)[2], auto last_c) {
-    if constexpr (decltype(last_c)::value) {
-      if (kblk + 32 > Ltot) {
+  // Keys past the end of the last tile score -inf.
+  auto mask_tail = [&](f32x16& s, int kblk) {
+    if (kblk + 32 > Ltot) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (kblk + key_of(v, hf) >= Ltot) s[v] = -INFINITY;
+      for (int v = 0; v < 16; ++v)
+        if (kblk + key_of(v, hf) >= Ltot) s[v] = -INFINITY;
+    }
+  };
+  // Lazy max, checked after the exponentials: they are taken against the
+  // running max, and only when some probability may exceed 2^8 (a lane's sum
+  // above 2^7 covers it, bf16 rounding included; a NaN sum, from the first
+  // unit's infinite max, too) does the wave take the block's exact max.  Where
+  // that lies more than 2^8 above the running max, the max is raised, the
+  // output accumulators (which already hold the previous unit's value
+  // product), the denominator and the S-CAS sums are rescaled, and the unit's
+  // exponentials are taken again.
+  auto settle = [&](const f32x16& s, Vec16 (&p)[2], float& psum) {
+    if (__builtin_expect(__any(!(psum <= kSumTrigger)), 0)) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t = fmaxf(t, s[v]);
+      t = fmaxf(t, __shfl_xor(t, 32));
+      const float mt = t * c2;
+      if (__any(mt > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] *= corr;
+        if constexpr (SCAS) scas_rescale(sa, corr);
+        psum = exp_pack<SCAS>(s, c2, m_run, p);
       }
     }
-    float t = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) t = fmaxf(t, s[v]);
-    t = fmaxf(t, __shfl_xor(t, 32));
-    const float mt = t * c2;
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= corr;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] *= corr;
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x = pprev[half].w[w];
-          pprev[half].w[w] = pack_bf16x2(bf16_lo(x) * corr, bf16_hi(x) * corr);
-        }
-      if constexpr (SCAS) {
-        scas_rescale(sa, corr);
-      }
-    }
+    l_run += psum;
   };
   // One pipelined step in 16 fixed slots: slot i issues the LDS read of the
   // fragment two slots ahead, one MFMA (value product of the previous unit in
@@ -705,7 +723,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if constexpr (first < last) fr[first % 3] = frag(first);
     if constexpr (first + 1 < last) fr[(first + 1) % 3] = frag(first + 1);
     if constexpr (DO_QK) snext = f32x16{};
-    float psum = 0.f, l1 = 0.f;
+    float psum = 0.f, l1 = 0.f, e[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i >= first && i < last) {
@@ -719,13 +737,13 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      s[i] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_run));
+      e[i & 1] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_run));
       if (i & 1) {
         const int half = i >> 3, w = (i & 7) >> 1;
-        p[half].w[w] = pack_bf16x2(s[i - 1], s[i]);
+        p[half].w[w] = pack_bf16x2(e[0], e[1]);
         if constexpr (SCAS) {
-          psum += s[i - 1];
-          l1 += s[i];
+          psum += e[0];
+          l1 += e[1];
         } else {
           if (w & 1) l1 = add_bf16x2(p[half].w[w], l1);
           else psum = add_bf16x2(p[half].w[w], psum);
@@ -733,9 +751,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    psum += l1;
-    l_run += psum;
-    return psum;
+    return psum + l1;
   };
 
   u32x4 reg[4];  // K(t+2) on waves 4-7, V(t+1) on waves 0-3
@@ -781,17 +797,19 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     }
 
     // step a: unit (t, keys 0..31)
-    front(s0, k0, p1, last_c);
-    const float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
-                          std::true_type{}, s0, p0);
-    if constexpr (SCAS) scas_block(a, hd, hf, s0, e0, k0, sa);
+    if constexpr (LAST) mask_tail(s0, k0);
+    float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
+                    std::true_type{}, s0, p0);
+    settle(s0, p0, e0);
+    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
     __syncthreads();
 
     // step b: unit (t, keys 32..63)
-    front(s1, k0 + 32, p0, last_c);
-    const float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
-                          std::integral_constant<bool, !LAST>{}, s1, p1);
-    if constexpr (SCAS) scas_block(a, hd, hf, s1, e1, k0 + 32, sa);
+    if constexpr (LAST) mask_tail(s1, k0 + 32);
+    float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
+                    std::integral_constant<bool, !LAST>{}, s1, p1);
+    settle(s1, p1, e1);
+    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
     bk = bn;
   };
   using T_ = std::true_type;

@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--pruned-steps", type=int, default=5)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
+    ap.add_argument("--data-sensitivity", action="store_true",
+                    help="time the final-scale attend launch of the main workload on its random "
+                         "inputs, with V zeroed, and with K and V zeroed (same instructions, less "
+                         "operand toggling), then exit")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -150,6 +154,44 @@ def lenb_table(keep, tokens):
     return f
 
 
+def data_sensitivity(ctx, wl, qs, kall, vall, outs, stream, torch, reps=20):
+    """Average duration of the final-scale attend launch (HIP events) when
+    the cache and the current scale hold the workload's random values, zero
+    values, or zero keys and values: the instruction stream is the same, only
+    the operands the matrix cores see toggle less."""
+    K, L = wl.n_scales, wl.layers
+    res = {}
+    for mode in ("random", "v_zero", "kv_zero", "random_again"):
+        ks = [k.clone() for k in kall]
+        vs = [v.clone() for v in vall]
+        if mode in ("v_zero", "kv_zero"):
+            for v in vs:
+                v.zero_()
+        if mode == "kv_zero":
+            for k in ks:
+                k.zero_()
+        ctx.reset()
+        for t in range(K - 1):
+            for l in range(L):
+                ctx.attend_append(l, t, qs[t][l], ks[t][l], vs[t][l], outs[t], wl.softmax_scale,
+                                  stream=stream)
+        last = lambda: ctx.attend(0, K - 1, qs[K - 1][0], ks[K - 1][0], vs[K - 1][0], outs[K - 1],  # noqa
+                                  wl.softmax_scale, stream=stream)
+        for _ in range(3):
+            last()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            last()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[mode] = round(e0.elapsed_time(e1) / reps * 1e3, 1)
+    return {"data_sensitivity": {"workload": wl.name, "launch": "final-scale attend, layer 0",
+                                 "avg_us": res, "reps": reps}}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -197,6 +239,9 @@ def main():
         outs.append(torch.empty_like(qs[-1][0]))
     flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
     total_flops = sum(flops.values())
+    if args.data_sensitivity:
+        print(json.dumps(data_sensitivity(ctx, wl, qs, kall, vall, outs, stream, torch)), flush=True)
+        return
 
     def one_pass(rec=None):
         """One generation pass: attention of every (layer, scale) with the

@@ -37,7 +37,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 ATTEND_SOURCES = ["kv_cache_compression_attend_amd/csrc/attend_bf16.hip",
                   "kv_cache_compression_attend_amd/csrc/attend.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_q256_infinity2b_layer_traffic.json")
-ROOFLINE_KERNEL = "attend_q256_kernel<false>"
+ROOFLINE_KERNEL = "attend_q256_kernel<false, false>"
 
 
 def attend_sources_sha() -> str:
@@ -59,6 +59,10 @@ def parse():
     ap.add_argument("--pruned-steps", type=int, default=5)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print the average duration of the final-scale attend launch (the "
+                         "largest-grid dispatches of the roofline kernel) from a rocprofv3 "
+                         "kernel-trace CSV of this benchmark, then exit")
     ap.add_argument("--data-sensitivity", action="store_true",
                     help="time the final-scale attend launch of the main workload on its random "
                          "inputs, with V zeroed, and with K and V zeroed (same instructions, less "
@@ -72,6 +76,26 @@ def parse():
     return ap.parse_args()
 
 
+def summarize_trace(path):
+    """Average duration of the final-scale launches of the roofline kernel in
+    a rocprofv3 kernel trace (the kernel also serves smaller scales, whose
+    dispatches have smaller grids)."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if ROOFLINE_KERNEL in r["Kernel_Name"]:
+                grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                rows.append((grid, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    if not rows:
+        raise SystemExit(f"no {ROOFLINE_KERNEL} dispatch in {path}")
+    top = max(g for g, _ in rows)
+    durs = [d for g, d in rows if g == top]
+    return {"kernel": ROOFLINE_KERNEL, "grid_threads": top, "dispatches": len(durs),
+            "avg_ns": round(sum(durs) / len(durs), 1), "min_ns": min(durs), "max_ns": max(durs),
+            "other_dispatches_of_kernel": len(rows) - len(durs)}
+
+
 def summarize_counters(paths):
     """Traffic profile (bytes per launch) of the final-scale attend launch of
     the default workload: FETCH_SIZE and WRITE_SIZE averaged over its
@@ -80,17 +104,22 @@ def summarize_counters(paths):
     import csv
 
     def per_dispatch(path, match):
-        vals = {}
+        vals, grid = {}, {}
         with open(path) as f:
             for r in csv.DictReader(f):
                 if match(r["Kernel_Name"]):
                     vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+                    grid[r["Dispatch_Id"]] = int(r["Grid_Size"])
         if not vals:
             raise SystemExit(f"no matching dispatch in {path}")
-        return sum(vals.values()) / len(vals), len(vals)
+        # The kernel also serves smaller scales: keep the final-scale
+        # dispatches, those with the largest grid.
+        top = max(grid.values())
+        keep = [d for d in vals if grid[d] == top]
+        return sum(vals[d] for d in keep) / len(keep), len(keep)
 
     def is_kernel(name):
-        return "attend_q256_kernel<false>" in name
+        return ROOFLINE_KERNEL in name
 
     def is_copy(name):
         return "copyBuffer" in name
@@ -196,6 +225,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.summarize_trace:
+        print(json.dumps(summarize_trace(args.summarize_trace), indent=1))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -308,8 +340,10 @@ def main():
     attend_total_ms = sum(attend_ms.values())
     attend_tflops = total_flops / (attend_total_ms * 1e-3) / 1e12
     n_launch = len(attend_ms)
-    # Launches served by the 256-query pipelined kernel (no split, no merge).
-    q256 = [key for key in attend_ms if ctx.attend_plan(key[2]) == (256, 1)]
+    # The dominant launch: the final scale, served by the 256-query pipelined
+    # kernel without a split.
+    q256 = [("a", l, K - 1) for l in range(L)]
+    assert all(ctx.attend_plan(K - 1) == (256, 1) for _ in q256), ctx.attend_plan(K - 1)
     q256_ms = sum(attend_ms[k] for k in q256)
     q256_flops = sum(flops[(k[1], k[2])] for k in q256)
     q256_tflops = q256_flops / (q256_ms * 1e-3) / 1e12 if q256 else 0.0

@@ -25,6 +25,7 @@ struct AttendArgs {
   float* ws_o;            // split launches: unnormalised outputs [n_split][B][n][H][D] fp32
   float2* ws_ml;          // split launches: (running max, denominator) [n_split][B][n][H]
   int B, H, n, K, step, n_qtiles;
+  int rows;               // bf16: query rows per workgroup (128 or 256)
   int n_split;            // key-range splits per query tile (1: no split)
   int append;             // 1: q-tile-0 workgroups also write this scale's kept
                           // K/V rows into the cache (fused append)
@@ -42,18 +43,24 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
-// Query rows per workgroup the bf16 attend launch uses for a scale of n
-// tokens (128 or 256); the S-CAS partial rows follow the same tiling.
-int attend_bf16_rows_per_workgroup(int B, int H, int n);
+// Query rows per workgroup (128 or 256) and key-range splits of one bf16
+// attend launch.
+struct AttendPlan {
+  int rows;
+  int splits;
+};
 
-// Key-range splits for a bf16 attend launch without S-CAS: 1 when the
-// launch fills the chip, else enough splits to give the 256 CUs two
-// workgroups each, keeping at least 4 key tiles per split of the longest head.
-int attend_bf16_splits(int B, int H, int n, int max_keys);
+// The plan for a scale of n tokens whose longest head holds max_keys keys
+// (its cached rows plus the scale's own): the (rows, splits) pair of least
+// modelled time.  The model counts launch rounds (one 256-query workgroup or
+// two 128-query workgroups per CU), key tiles per split plus a per-workgroup
+// set-up cost, and the merge of split partials.  allow_split false (S-CAS
+// launches) keeps one split.
+AttendPlan attend_bf16_plan(int B, int H, int n, int max_keys, bool allow_split);
 
-// Launchers (defined next to their kernels).  a.n_qtiles must follow
-// attend_bf16_rows_per_workgroup and a.n_split attend_bf16_splits (or 1)
-// for the bf16 launch; a split launch also merges the splits into a.out.
+// Launchers (defined next to their kernels).  For the bf16 launch a.rows,
+// a.n_split and a.n_qtiles = ceil(n / rows) follow an attend_bf16_plan (S-CAS
+// launches: one split); a split launch also merges the splits into a.out.
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s);
 hipError_t launch_attend_f32(const AttendArgs& a, int D, bool scas, hipStream_t s);
 

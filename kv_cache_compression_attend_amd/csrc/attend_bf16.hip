@@ -44,11 +44,14 @@
 //     workgroup into one partial row per workgroup; a second kernel adds the
 //     partials in a fixed order (no float atomics, deterministic).
 //
-// Two tilings:
+// Two tilings, chosen per launch by a cost model (attend_bf16_plan):
 //   * 128 queries per workgroup of 4 waves, two workgroups per CU; the 64-key
-//     tile is scored, normalised and accumulated in sequence.  Used when the
-//     launch is too small to fill the chip with 256-query workgroups.
-//   * 256 queries per workgroup of 8 waves (two per SIMD).  Per 32-key unit u
+//     tile is scored, normalised and accumulated in sequence.  Used for the
+//     smallest launches and for S-CAS launches that would not fill the chip
+//     with 256-query workgroups.
+//   * 256 queries per workgroup of 8 waves (two per SIMD), optionally with
+//     each head's key range split over several workgroups whose (output,
+//     max, denominator) partials a merge kernel combines.  Per 32-key unit u
 //     a wave runs the score product QK(u) (8 MFMAs), the softmax SM(u) and
 //     the value product PV(u) (8 MFMAs), pipelined as step
 //     i = { PV(u_{i-1}), QK(u_{i+1}) } on the matrix cores beside SM(u_i) on
@@ -61,6 +64,8 @@
 //     first and last tiles are separate instantiations, so the steady-state
 //     step is straight-line code.
 #include <math.h>
+
+#include <algorithm>
 
 #include <type_traits>
 
@@ -109,8 +114,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // acc + lo(w) + hi(w), the two bf16 halves of w summed in fp32.
 __device__ __forceinline__ float add_bf16x2(uint32_t w, float acc) {
@@ -304,6 +307,22 @@ struct ProbOf {
   }
 };
 
+// A split's unnormalised output row (fp32) and its (running max, denominator)
+// into the split workspace, for attend_combine_kernel.
+__device__ __forceinline__ void write_split(const AttendArgs& a, const Head& hd, int qrow, int hf,
+                                            const f32x16 (&o)[4], float m, float l) {
+  if (qrow >= hd.n) return;
+  const int64_t row = (int64_t(hd.split) * a.B + hd.b) * hd.n * a.H + int64_t(qrow) * a.H + hd.h;
+  float* op = a.ws_o + row * D;
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp)
+      *reinterpret_cast<float4*>(op + 32 * db + 8 * kp + 4 * hf) =
+          make_float4(o[db][4 * kp], o[db][4 * kp + 1], o[db][4 * kp + 2], o[db][4 * kp + 3]);
+  if (hf == 0) a.ws_ml[row] = make_float2(m, l);
+}
+
 // Adds this lane's probabilities of keys [kblk, kblk + 32) to the
 // accumulator of every source segment they fall in.  Source src < step
 // covers cache rows [lenb[src], lenb[src+1]); the current scale covers
@@ -447,11 +466,9 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
   const float c2 = a.scale_log2;
-  // Key tiles [t_lo, t_hi) of this workgroup's split.
-  const int ntiles_all = (Ltot + BN - 1) / BN;
-  const int per_split = (ntiles_all + a.n_split - 1) / a.n_split;
-  const int t_lo = hd.split * per_split;
-  const int t_hi = min(ntiles_all, t_lo + per_split);
+  // Key tiles [t_lo, t_hi): this tiling is never split.
+  const int t_lo = 0;
+  const int t_hi = (Ltot + BN - 1) / BN;
 
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
@@ -555,23 +572,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     __syncthreads();
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (a.n_split > 1) {
-    // Unnormalised output and (max, denominator) of this split, merged later.
-    if (qrow < hd.n) {
-      const int64_t row = (int64_t(hd.split) * a.B + hd.b) * hd.n * a.H + int64_t(qrow) * a.H + hd.h;
-      float* op = a.ws_o + row * D;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kp = 0; kp < 4; ++kp)
-          *reinterpret_cast<float4*>(op + 32 * db + 8 * kp + 4 * hf) =
-              make_float4(oacc[db][4 * kp], oacc[db][4 * kp + 1], oacc[db][4 * kp + 2], oacc[db][4 * kp + 3]);
-      if (hf == 0) a.ws_ml[row] = make_float2(m_run, l_tot);
-    }
-    return;
-  }
-  const float inv = 1.f / l_tot;
+  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
   store_out(a, hd, qrow, hf, oacc, inv);
   if constexpr (SCAS) {
     scas_flush(sa);
@@ -611,7 +612,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // ---------------------------------------------------------------------------
 // 256 queries per workgroup of 8 waves, 32 per wave, software-pipelined.
 // ---------------------------------------------------------------------------
-template <bool SCAS>
+// SPLIT: the launch splits each head's key range (a.n_split > 1); a separate
+// instantiation, so the unsplit kernel carries no split code.
+template <bool SCAS, bool SPLIT>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[3][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3][D * VSTR];
@@ -636,8 +639,18 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
-  const int ntiles = (Ltot + BN - 1) / BN;
   const float c2 = a.scale_log2;
+  // Key tiles [t_lo, t_hi) of this workgroup's split.
+  const int ntiles_all = (Ltot + BN - 1) / BN;
+  const int per_split = SPLIT ? (ntiles_all + a.n_split - 1) / a.n_split : ntiles_all;
+  const int t_lo = SPLIT ? hd.split * per_split : 0;
+  const int t_hi = SPLIT ? min(ntiles_all, t_lo + per_split) : ntiles_all;
+  if (SPLIT && t_lo >= t_hi) {
+    // A head with fewer key tiles than splits: an empty partial (weight 0 in
+    // the merge).  The whole workgroup leaves before any barrier.
+    write_split(a, hd, qrow, hf, o, -INFINITY, 0.f);
+    return;
+  }
 
   auto qk = [&](const uint16_t* Kt, int kb, f32x16& s) {
     s = f32x16{};
@@ -760,23 +773,26 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) p1[half].u = u32x4{0, 0, 0, 0};
 
-  // Prologue: K(0) in buffer 0; K(1) (waves 4-7) and V(0) (waves 0-3) in registers.
+  // Prologue: K(t_lo) in buffer 0; K(t_lo + 1) (waves 4-7) and V(t_lo)
+  // (waves 0-3) in registers.  Every split holds at least one tile.
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
+  const int k_lo = t_lo * BN;
   if (kstager) {
-    load_k(hd.ks, 0, stid, reg);
+    load_k(hd.ks, k_lo, stid, reg);
     store_k(sK[0], stid, reg);
-    if (hd.append) append_rows(hd.ks, kc_w, 0, stid >> 4, 16, stid & 15, reg);
-    if (ntiles > 1) load_k(hd.ks, BN, stid, reg);
+    if (hd.append) append_rows(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
+    if (t_lo + 1 < t_hi) load_k(hd.ks, k_lo + BN, stid, reg);
   } else {
-    load_v(hd.vs, 0, stid, reg);
+    load_v(hd.vs, k_lo, stid, reg);
   }
   __syncthreads();
   qk(sK[0], 0, s0);
 
-  // One 64-key tile; FIRST drops the value product of the absent previous
-  // unit, LAST the score product of the absent next tile and enables the
-  // tail mask.
+  // One 64-key tile; FIRST (the split's first tile) drops the value product
+  // of the absent previous unit, LAST (its last) the score product of the
+  // absent next tile and enables the tail mask, which only the head's final
+  // tile needs.
   int bk = 0;  // LDS buffer of K(t) and of V(t)
   auto tile = [&](int t, auto first_c, auto last_c) {
     constexpr bool FIRST = decltype(first_c)::value;
@@ -789,7 +805,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
         store_k(sK[bn], stid, reg);
         if (hd.append) append_rows(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
       }
-      if (t + 2 < ntiles) load_k(hd.ks, k0 + 2 * BN, stid, reg);
+      if (t + 2 < t_hi) load_k(hd.ks, k0 + 2 * BN, stid, reg);
     } else {
       store_v(sV[bk], stid, reg);
       if (hd.append) append_rows(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
@@ -814,16 +830,22 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (ntiles == 1) {
-    tile(0, T_{}, T_{});
+  if (t_hi - t_lo == 1) {
+    tile(t_lo, T_{}, T_{});
   } else {
-    tile(0, T_{}, F_{});
-    for (int t = 1; t + 1 < ntiles; ++t) tile(t, F_{}, F_{});
-    tile(ntiles - 1, F_{}, T_{});
+    tile(t_lo, T_{}, F_{});
+    for (int t = t_lo + 1; t + 1 < t_hi; ++t) tile(t, F_{}, F_{});
+    tile(t_hi - 1, F_{}, T_{});
   }
   pv(sV[bk == 0 ? 2 : bk - 1], 1, p1);
 
-  const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if constexpr (SPLIT) {
+    // Unnormalised output and (max, denominator) of this split, merged later.
+    write_split(a, hd, qrow, hf, o, m_run, l_tot);
+    return;
+  }
+  const float inv = 1.f / l_tot;
   store_out(a, hd, qrow, hf, o, inv);
   if constexpr (SCAS) {
     scas_flush(sa);
@@ -833,42 +855,57 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 
 }  // namespace
 
-// 256-query workgroups (one per CU) when they fill at least one full round of
-// the 256 CUs; otherwise 128-query workgroups (two per CU), which spread a
-// small launch over more CUs.
-int attend_bf16_rows_per_workgroup(int B, int H, int n) {
-  const int64_t wg256 = int64_t(B) * H * ((n + 255) / 256);
-  return wg256 >= 256 ? 256 : 128;
-}
+// Plan model, in microseconds, fitted to every (rows, splits) choice for
+// scales 2-11 of the 16-head full-cache layer at batch 1 and 8 on the MI355X
+// (random bf16 data): a 64-key tile of a 256-query workgroup (one resident
+// per CU) takes kTile256, of a 128-query workgroup (two resident per CU)
+// kTile128; a workgroup's set-up (query load, first staging) adds kSetup*
+// tiles; a split launch adds the merge, kMerge plus kMergeRow per partial
+// output row.  Costs common to every choice (the launch) are left out.
+namespace {
+constexpr double kTile256 = 1.80;
+constexpr double kTile128 = 2.00;
+constexpr double kSetup256 = 0.17;
+constexpr double kSetup128 = 0.0;
+constexpr double kMerge = 3.15;
+constexpr double kMergeRow = 0.00024;
+constexpr int kMaxSplits = 16;
+constexpr int kMinTilesPerSplit = 2;
+}  // namespace
 
-int attend_bf16_splits(int B, int H, int n, int max_keys) {
-  if (attend_bf16_rows_per_workgroup(B, H, n) != 128) return 1;
-  const int64_t wg = int64_t(B) * H * ((n + 127) / 128);
-  const int tiles = (max_keys + BN - 1) / BN;
-  // Rounds of 512 workgroup slots (two per CU) per unit of work, plus a small
-  // per-split cost for the merge.
-  int best = 1;
-  double best_cost = 1e30;
-  for (int sp = 1; sp <= 16; ++sp) {
-    if (sp > 1 && tiles < 4 * sp) break;
-    const double rounds = double((wg * sp + 511) / 512);
-    const double cost = rounds / sp + 0.03 * (sp - 1);
-    if (cost < best_cost - 1e-9) {
-      best_cost = cost;
-      best = sp;
+AttendPlan attend_bf16_plan(int B, int H, int n, int max_keys, bool allow_split) {
+  const int tiles = std::max(1, (max_keys + BN - 1) / BN);
+  AttendPlan best{256, 1};
+  double best_cost = 1e300;
+  for (const int rows : {256, 128}) {
+    const int64_t wg = int64_t(B) * H * ((n + rows - 1) / rows);
+    const int64_t slots = rows == 256 ? 256 : 512;
+    const double tile_us = rows == 256 ? kTile256 : kTile128;
+    const double setup = rows == 256 ? kSetup256 : kSetup128;
+    for (int sp = 1; sp <= (rows == 256 ? kMaxSplits : 1); ++sp) {
+      if (sp > 1 && (!allow_split || tiles < kMinTilesPerSplit * sp)) break;
+      const double rounds = double((wg * sp + slots - 1) / slots);
+      const double per_split = double((tiles + sp - 1) / sp);
+      double cost = rounds * (per_split + setup) * tile_us;
+      if (sp > 1) cost += kMerge + kMergeRow * double(sp) * B * n * H;
+      if (cost < best_cost * (1 - 1e-9)) {
+        best_cost = cost;
+        best = AttendPlan{rows, sp};
+      }
     }
   }
   return best;
 }
 
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
-  const int rows = attend_bf16_rows_per_workgroup(a.B, a.H, a.n);
+  const int rows = a.rows;
   const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
-  if (a.n_qtiles != (a.n + rows - 1) / rows) return hipErrorInvalidValue;
-  if (a.n_split < 1 || (a.n_split > 1 && (scas || rows != 128 || !a.ws_o || !a.ws_ml)))
+  if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows)
+    return hipErrorInvalidValue;
+  if (a.n_split < 1 || (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
     return hipErrorInvalidValue;
   if (a.n_split > 1) {
-    hipLaunchKernelGGL(attend_q128_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attend_q256_kernel<false, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t out_rows = int64_t(a.B) * a.n * a.H;
@@ -878,9 +915,9 @@ hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s
   }
   if (rows == 256) {
     if (scas)
-      hipLaunchKernelGGL(attend_q256_kernel<true>, dim3(unsigned(blocks)), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attend_q256_kernel<true, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL(attend_q256_kernel<false>, dim3(unsigned(blocks)), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attend_q256_kernel<false, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
   } else {
     if (scas)
       hipLaunchKernelGGL(attend_q128_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a);

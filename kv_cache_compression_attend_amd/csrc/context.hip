@@ -42,7 +42,9 @@ struct hk_ctx {
   hk::GatherRun* d_gruns = nullptr;
   int64_t* d_rowdst = nullptr;    // [K][L][H] byte offset where (l, h) stores scale t, or -1
   float* d_partials = nullptr;
+  std::vector<int> rows;          // [K] query rows per workgroup of each scale's attend launch
   std::vector<int> splits;        // [K] key-range splits of each scale's attend launch
+  std::vector<int> rows_scas;     // [K] query rows per workgroup with S-CAS (never split)
   float* d_ws_o = nullptr;        // split workspace: unnormalised outputs
   float2* d_ws_ml = nullptr;      // split workspace: (max, denominator)
   std::vector<int> appended;      // last scale appended per layer (-1: none)
@@ -121,11 +123,6 @@ void free_tables(hk_ctx* c) {
   c->d_partials = nullptr;
 }
 
-// Query rows per attend workgroup.
-int rows_per_workgroup(int dtype, int B, int H, int n) {
-  return dtype == HK_DTYPE_BF16 ? hk::attend_bf16_rows_per_workgroup(B, H, n) : 64;
-}
-
 template <typename T>
 hipError_t upload(T** dst, const std::vector<T>& src) {
   const size_t bytes = std::max<size_t>(src.size(), 1) * sizeof(T);
@@ -194,14 +191,14 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.partials = c->d_partials;
   a.ws_o = c->d_ws_o;
   a.ws_ml = c->d_ws_ml;
+  a.rows = scas ? c->rows_scas[step] : c->rows[step];
   a.n_split = scas ? 1 : c->splits[step];
   a.B = c->B;
   a.H = c->H;
   a.n = c->tokens[step];
   a.K = c->K;
   a.step = step;
-  const int rows = rows_per_workgroup(c->dtype, c->B, c->H, a.n);
-  a.n_qtiles = (a.n + rows - 1) / rows;
+  a.n_qtiles = (a.n + a.rows - 1) / a.rows;
   a.scale = softmax_scale;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   // bf16 kernels append in the same launch, unless segments leave at this
@@ -443,26 +440,29 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
     }
   }
 
-  int64_t max_partials = 1;
-  for (int t = 0; t < K; ++t) {
-    const int rows = rows_per_workgroup(dtype, B, H, scale_tokens[t]);
-    const int64_t qt = (scale_tokens[t] + rows - 1) / rows;
-    max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
-  }
-
-  // Key-range splits per scale (bf16 launches without S-CAS that would not
-  // fill the chip) and the workspace the largest split launch needs.
+  // Attend plans per scale: query rows per workgroup and key-range splits
+  // (bf16 launches without S-CAS may split the keys of a launch that would
+  // not fill the chip), the S-CAS partial rows and the split workspace the
+  // largest launch needs.  fp32 launches take 64 query rows, unsplit.
+  c->rows.assign(K, 64);
+  c->rows_scas.assign(K, 64);
   c->splits.assign(K, 1);
+  int64_t max_partials = 1;
   int64_t ws_rows = 0;
-  if (dtype == HK_DTYPE_BF16) {
-    for (int t = 0; t < K; ++t) {
+  for (int t = 0; t < K; ++t) {
+    if (dtype == HK_DTYPE_BF16) {
       int max_keys = 0;
       for (int64_t f = 0; f < heads; ++f)
         max_keys = std::max<int>(max_keys, lenb_at(t, f, t) + scale_tokens[t]);
-      c->splits[t] = hk::attend_bf16_splits(B, H, scale_tokens[t], max_keys);
-      if (c->splits[t] > 1)
-        ws_rows = std::max<int64_t>(ws_rows, int64_t(c->splits[t]) * B * scale_tokens[t] * H);
+      const hk::AttendPlan p = hk::attend_bf16_plan(B, H, scale_tokens[t], max_keys, true);
+      c->rows[t] = p.rows;
+      c->splits[t] = p.splits;
+      c->rows_scas[t] = hk::attend_bf16_plan(B, H, scale_tokens[t], max_keys, false).rows;
+      if (p.splits > 1)
+        ws_rows = std::max<int64_t>(ws_rows, int64_t(p.splits) * B * scale_tokens[t] * H);
     }
+    const int64_t qt = (scale_tokens[t] + c->rows_scas[t] - 1) / c->rows_scas[t];
+    max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
   }
 
   hipError_t e = hipGetDevice(&c->device);
@@ -731,7 +731,7 @@ extern "C" int hk_attend_plan(const hk_ctx* c, int step, int with_scas, int32_t*
                               int32_t* splits) {
   if (!c || !rows_per_wg || !splits) return fail(HK_EINVAL, "null argument");
   if (step < 0 || step >= c->K) return fail(HK_EINVAL, "step %d out of [0, %d)", step, c->K);
-  *rows_per_wg = rows_per_workgroup(c->dtype, c->B, c->H, c->tokens[step]);
+  *rows_per_wg = with_scas ? c->rows_scas[step] : c->rows[step];
   *splits = with_scas ? 1 : c->splits[step];
   return HK_OK;
 }

@@ -444,3 +444,28 @@ def test_order_and_argument_errors():
     assert ctx.retained_tokens(0) == 2 and ctx.retained_tokens(2) == 2 * (1 + 4)
     torch.cuda.synchronize()
     ctx.close()
+
+
+def test_split_launch_with_empty_splits():
+    """A 256-query launch whose keys are split over several workgroups, where
+    one head holds so few keys that some of its splits are empty (their
+    partials carry zero weight in the merge); every head against the oracle,
+    plain and fused."""
+    wl = _custom(91, "split-empty", (1, 2, 3, 4, 6, 8, 12, 16, 24), heads=3, head_dim=128, batch=1,
+                 dtype="bf16")
+    keep = np.ones((1, wl.heads, wl.n_scales), dtype=np.uint8)
+    keep[:, :, -1] = 0
+    keep[0, 2, 1:] = 0          # head 2 keeps the sink only
+    keep[0, 1, 3:6] = 0         # head 1 drops a middle run
+    for fused in (False, True):
+        run = generate(wl, keep, [0], fused=fused)
+        last = wl.n_scales - 1
+        rows, splits = run.ctx.attend_plan(last)
+        assert rows == 256 and splits > 1, (rows, splits)
+        keys_short = 1 + wl.scale_tokens[last]
+        tiles = -(-keys_short // 64)
+        per = -(-tiles // splits)
+        assert (splits - 1) * per >= tiles, "no empty split for the short head"
+        _compare_outputs(run, [0], rows_per_unit=256)
+        check_cache(run, [0])
+        run.ctx.close()

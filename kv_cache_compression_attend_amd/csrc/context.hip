@@ -663,17 +663,18 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n_desc = int(glast - gfirst);
     a.B = c->B;
     a.row_bytes = c->D * c->elem_bytes;
-    a.rows_per_chunk = 32768 / a.row_bytes;  // 8 vectors per lane per tensor
+    a.rows_per_chunk = hk::kGatherChunkBytes / a.row_bytes;
     hipError_t e = hk::launch_gather(a, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }
   const int row_bytes = c->D * c->elem_bytes;
-  const int rows_per_block = 32768 / row_bytes;
-  if (last > first && 2 * (last - first) >= int64_t(nl) * c->H && c->tokens[step] < rows_per_block) {
+  const int rows_per_block = hk::kCopyBlockBytes / row_bytes;
+  if (last > first && 2 * (last - first) >= int64_t(nl) * c->H &&
+      c->tokens[step] < hk::kTokenBlockBytes / row_bytes) {
     // A short scale that most heads store: per-head workgroups would each
-    // move less than one 32 KB block, so copy whole token blocks instead
-    // (contiguous reads, every head's rows written from one workgroup).  On
-    // long scales the per-head copy is faster (one contiguous write stream).
+    // move little, so copy whole token blocks instead (contiguous reads,
+    // every head's rows written from one workgroup).  On long scales the
+    // per-head copy is faster (one contiguous write stream).
     DeviceGuard g(c->device);
     if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
     hk::RowsArgs a{};
@@ -689,7 +690,7 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n = c->tokens[step];
     a.H = c->H;
     a.row_bytes = row_bytes;
-    a.rows = std::max(1, 32768 / (c->H * row_bytes));   // 32 KB per tensor per workgroup
+    a.rows = std::max(1, hk::kCopyBlockBytes / (c->H * row_bytes));   // one block per tensor
     hipError_t e = hk::launch_compact_rows(a, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "compact launch");
   } else if (last > first) {
@@ -707,8 +708,12 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n = c->tokens[step];
     a.H = c->H;
     a.row_bytes = c->D * c->elem_bytes;
-    // 2048 16-byte vectors per tensor per workgroup: 8 per lane.
-    a.rows_per_block = std::min(std::max(1, rows_per_block), a.n);
+    // One block per tensor per workgroup; the large block when the launch
+    // has enough of them.
+    const int large_rows = hk::kCopyBlockBytesLarge / row_bytes;
+    const int64_t large_blocks = (last - first) * c->B * ((a.n + large_rows - 1) / large_rows);
+    const int block_rows = large_blocks >= hk::kCopyLargeMinBlocks ? large_rows : rows_per_block;
+    a.rows_per_block = std::min(std::max(1, block_rows), a.n);
     a.chunks = (a.n + a.rows_per_block - 1) / a.rows_per_block;
     a.layer_begin = layer_begin;
     hipError_t e = hk::launch_compact(a, static_cast<hipStream_t>(hip_stream));

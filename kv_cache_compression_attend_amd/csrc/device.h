@@ -9,6 +9,22 @@
 
 namespace hk {
 
+// Copy geometry shared by the compaction kernels and the host code that
+// sizes their grids: a workgroup of kCopyThreads lanes moves one block per
+// tensor in a single pass, kCopyBlockBytes (4 16-byte vectors per lane in
+// flight) or kCopyBlockBytesLarge (8).  Measured on the MI355X: 4 per lane is
+// the fastest plain contiguous copy and the faster compaction of launches
+// with few head runs; 8 per lane the faster one when a launch has at least
+// kCopyLargeMinBlocks blocks of the large size.  The in-place gather walks its
+// region in kGatherChunkBytes chunks, one pass each.  Scales shorter than
+// kTokenBlockBytes per head that most heads store are copied in token blocks.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyBlockBytes = 16384;
+constexpr int kCopyBlockBytesLarge = 32768;
+constexpr int64_t kCopyLargeMinBlocks = 16384;
+constexpr int kGatherChunkBytes = 32768;
+constexpr int kTokenBlockBytes = 32768;
+
 // One kept (layer, head) segment of a completed scale, to be copied into the cache.
 struct CopyDesc {
   int64_t dst;            // byte offset of row len_before(l,h,t) of (l,h,b=0)

@@ -244,12 +244,21 @@ __device__ __forceinline__ Head setup(const AttendArgs& a) {
   hd.vs = KeySource{static_cast<const char*>(a.vcache) + hb, static_cast<const char*>(a.vcur) + curoff,
                     hd.Lc, hd.Ltot, hd.n, hd.tokb};
   hd.q = static_cast<const char*>(a.q) + curoff;
-  // One workgroup per (b, h, split) appends: the one with q-tile 0.  A pruned
-  // segment (no cache rows reserved for this scale) is never written, and
-  // nothing is written past the head's capacity.
-  hd.append = a.append && hd.qt == 0 && a.step + 1 < a.K && hd.lenb[a.step + 1] > hd.Lc &&
+  // Every workgroup of a (b, h, split) stages all of its key tiles; the
+  // append of tile t falls to the one with q-tile t mod n_qtiles, so the
+  // writes are spread over the workgroups.  A pruned segment (no cache rows
+  // reserved for this scale) is never written, and nothing is written past
+  // the head's capacity.
+  hd.append = a.append && a.step + 1 < a.K && hd.lenb[a.step + 1] > hd.Lc &&
               hd.lenb[a.step + 1] <= cap;
   return hd;
+}
+
+// The first key tile at or after t whose append falls to this workgroup
+// (tiles t' with t' mod n_qtiles == q-tile); later ones follow every
+// n_qtiles tiles.
+__device__ __forceinline__ int first_append_tile(const AttendArgs& a, const Head& hd, int t) {
+  return t + (hd.qt - t % a.n_qtiles + a.n_qtiles) % a.n_qtiles;
 }
 
 // Q^T fragments of query qrow: dims 16*kk + 8*hf + [0, 8); zero past the end.
@@ -472,10 +481,12 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
-  auto append_tile = [&](int k0) {
-    if (hd.append) {
-      append_rows(hd.ks, kc_w, k0, tid >> 4, 16, tid & 15, kreg);
-      append_rows(hd.vs, vc_w, k0, 4 * (tid & 15), 1, tid >> 4, vreg);
+  int next_append = first_append_tile(a, hd, t_lo);
+  auto append_tile = [&](int t) {
+    if (hd.append && t == next_append) {
+      append_rows(hd.ks, kc_w, t * BN, tid >> 4, 16, tid & 15, kreg);
+      append_rows(hd.vs, vc_w, t * BN, 4 * (tid & 15), 1, tid >> 4, vreg);
+      next_append += a.n_qtiles;
     }
   };
 
@@ -484,7 +495,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     load_v(hd.vs, t_lo * BN, tid, vreg);
     store_k(sK[0], tid, kreg);
     store_v(sV[0], tid, vreg);
-    append_tile(t_lo * BN);
+    append_tile(t_lo);
     if (t_lo + 1 < t_hi) {
       load_k(hd.ks, (t_lo + 1) * BN, tid, kreg);
       load_v(hd.vs, (t_lo + 1) * BN, tid, vreg);
@@ -498,7 +509,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     if (it + 1 < t_hi) {
       store_k(sK[buf ^ 1], tid, kreg);
       store_v(sV[buf ^ 1], tid, vreg);
-      append_tile(k0 + BN);
+      append_tile(it + 1);
     }
     if (it + 2 < t_hi) {
       load_k(hd.ks, k0 + 2 * BN, tid, kreg);
@@ -778,10 +789,14 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
   const int k_lo = t_lo * BN;
+  // The first tile at or after the current one whose append falls to this
+  // workgroup; kept uniform (updated outside the stager branches) so that it
+  // stays in a scalar register.
+  int next_append = first_append_tile(a, hd, t_lo);
   if (kstager) {
     load_k(hd.ks, k_lo, stid, reg);
     store_k(sK[0], stid, reg);
-    if (hd.append) append_rows(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
+    if (hd.append && t_lo == next_append) append_rows(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
     if (t_lo + 1 < t_hi) load_k(hd.ks, k_lo + BN, stid, reg);
   } else {
     load_v(hd.vs, k_lo, stid, reg);
@@ -800,15 +815,18 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     const int k0 = t * BN;
     const int bn = bk == 2 ? 0 : bk + 1;
     const int bp = bk == 0 ? 2 : bk - 1;
+    const bool append_v = hd.append && t == next_append;  // V(t)
+    if (t == next_append) next_append += a.n_qtiles;
+    const bool append_k = hd.append && t + 1 == next_append;  // K(t + 1)
     if (kstager) {
       if constexpr (!LAST) {
         store_k(sK[bn], stid, reg);
-        if (hd.append) append_rows(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
+        if (append_k) append_rows(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
       }
       if (t + 2 < t_hi) load_k(hd.ks, k0 + 2 * BN, stid, reg);
     } else {
       store_v(sV[bk], stid, reg);
-      if (hd.append) append_rows(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
+      if (append_v) append_rows(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
       if constexpr (!LAST) load_v(hd.vs, k0 + BN, stid, reg);
     }
 

@@ -326,10 +326,11 @@ int hk_ranking_stability(int L, int H, int K, const int32_t* scale_tokens, const
 /* hk_attend (or, with scas_table != NULL, hk_attend_with_scas) of scale
  * `step` in `layer`, followed by hk_append_scale of the same scale and layer,
  * for callers that run the two back to back.  With bf16 both happen in one
- * launch: the workgroups of query tile 0, which stage every key and value of
- * the current scale anyway, also write the kept rows into the cache (rows
- * the launch itself never reads), so the scale is read from HBM once instead
- * of twice.  The final scale (step = K-1) is only attended.
+ * launch: every workgroup stages every key and value tile of its key range
+ * anyway, and the one with query tile (key tile mod query tiles) also writes
+ * that tile's kept current-scale rows into the cache (rows the launch itself
+ * never reads), so the scale is read from HBM once instead of twice.  The
+ * final scale (step = K-1) is only attended.
  * Order: as hk_attend, and the layer's last appended scale must be step-1.
  * Errors: as hk_attend. */
 int hk_attend_append(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,

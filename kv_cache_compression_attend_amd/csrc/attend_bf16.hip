@@ -86,6 +86,7 @@ constexpr int BN = 64;        // keys per staged tile
 constexpr int KSTR = D + 8;   // K tile row stride (bf16 elements): 272 bytes
 constexpr int VSTR = BN + 8;  // V^T tile row stride (bf16 elements): 144 bytes
 constexpr int kRowBytes = D * 2;
+constexpr int kMaxSplits = 16;  // key-range splits per head in one launch
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr float kSumTrigger = 128.f;   // 2^(kRescaleSlack - 1)
 constexpr unsigned kOutOfRange = 0x80000000u;
@@ -593,25 +594,41 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 
 // Merges the splits of one output row: with M the largest split max and
 // w_s = 2^(m_s - M), out = sum_s w_s O_s / sum_s w_s l_s, added in split
-// order.  32 lanes per row, 4 dims per lane.
+// order.  32 lanes per row, 4 dims per lane.  Every split's (max, sum) and
+// output slice are loaded before any is used, so a row costs one memory
+// latency rather than one per split; MAXS (>= n_split) bounds the registers
+// this takes.
+template <int MAXS>
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, const float2* ws_ml,
                                                              uint16_t* out, int64_t rows, int n_split) {
   const int64_t row = int64_t(blockIdx.x) * 8 + (threadIdx.x >> 5);
   if (row >= rows) return;
   const int d0 = 4 * (threadIdx.x & 31);
+  float2 ml[MAXS];
+  float4 o[MAXS];
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp) {
+    if (sp < n_split) {
+      ml[sp] = ws_ml[sp * rows + row];
+      o[sp] = *reinterpret_cast<const float4*>(ws_o + (sp * rows + row) * D + d0);
+    }
+  }
   float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ws_ml[sp * rows + row].x);
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp)
+    if (sp < n_split) M = fmaxf(M, ml[sp].x);
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float2 ml = ws_ml[sp * rows + row];
-    const float w = __builtin_amdgcn_exp2f(ml.x - M);
-    const float4 o = *reinterpret_cast<const float4*>(ws_o + (sp * rows + row) * D + d0);
-    L = fmaf(w, ml.y, L);
-    acc.x = fmaf(w, o.x, acc.x);
-    acc.y = fmaf(w, o.y, acc.y);
-    acc.z = fmaf(w, o.z, acc.z);
-    acc.w = fmaf(w, o.w, acc.w);
+#pragma unroll
+  for (int sp = 0; sp < MAXS; ++sp) {
+    if (sp < n_split) {
+      const float w = __builtin_amdgcn_exp2f(ml[sp].x - M);
+      L = fmaf(w, ml[sp].y, L);
+      acc.x = fmaf(w, o[sp].x, acc.x);
+      acc.y = fmaf(w, o[sp].y, acc.y);
+      acc.z = fmaf(w, o[sp].z, acc.z);
+      acc.w = fmaf(w, o[sp].w, acc.w);
+    }
   }
   const float inv = 1.f / L;
   uint2 wv;
@@ -887,7 +904,6 @@ constexpr double kSetup256 = 0.17;
 constexpr double kSetup128 = 0.0;
 constexpr double kMerge = 3.15;
 constexpr double kMergeRow = 0.00024;
-constexpr int kMaxSplits = 16;
 constexpr int kMinTilesPerSplit = 2;
 }  // namespace
 
@@ -920,15 +936,23 @@ hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s
   const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
   if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows)
     return hipErrorInvalidValue;
-  if (a.n_split < 1 || (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
+  if (a.n_split < 1 || a.n_split > kMaxSplits ||
+      (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
     return hipErrorInvalidValue;
   if (a.n_split > 1) {
     hipLaunchKernelGGL((attend_q256_kernel<false, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t out_rows = int64_t(a.B) * a.n * a.H;
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(unsigned((out_rows + 7) / 8)), dim3(256), 0, s,
-                       a.ws_o, a.ws_ml, static_cast<uint16_t*>(a.out), out_rows, a.n_split);
+    const dim3 grid(unsigned((out_rows + 7) / 8));
+    uint16_t* out = static_cast<uint16_t*>(a.out);
+    if (a.n_split <= 4)
+      hipLaunchKernelGGL(attend_combine_kernel<4>, grid, dim3(256), 0, s, a.ws_o, a.ws_ml, out, out_rows, a.n_split);
+    else if (a.n_split <= 8)
+      hipLaunchKernelGGL(attend_combine_kernel<8>, grid, dim3(256), 0, s, a.ws_o, a.ws_ml, out, out_rows, a.n_split);
+    else
+      hipLaunchKernelGGL(attend_combine_kernel<kMaxSplits>, grid, dim3(256), 0, s, a.ws_o, a.ws_ml, out,
+                         out_rows, a.n_split);
     return hipGetLastError();
   }
   if (rows == 256) {

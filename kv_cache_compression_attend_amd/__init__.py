@@ -25,8 +25,9 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 import torch  # first: the library binds to the HIP runtime torch has loaded
 
-__all__ = ["HeatKVError", "build_schedule", "layout", "scas_mean", "ranking_stability", "Context",
-           "library_path", "DTYPES"]
+__all__ = ["HeatKVError", "build_schedule", "build_progressive_schedule", "build_scale_window_schedule",
+           "cache_size_after_layer", "layout", "layout_expiry", "layout_int4", "scas_mean",
+           "ranking_stability", "Context", "library_path", "DTYPES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libheatkv.so")

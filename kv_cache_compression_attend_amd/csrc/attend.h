@@ -10,6 +10,14 @@ namespace hk {
 constexpr int kMaxScales = 16;   // S-CAS accumulators per query row
 constexpr int kXcds = 8;         // MI355X: 8 accelerator dies, 32 CUs each
 
+// A dispatch packet holds 32-bit grid sizes in work-items; launchers refuse
+// a grid that would not fit (hipErrorInvalidConfiguration) instead of
+// truncating it.  y and z stay within the runtime's 16-bit limits.
+inline bool grid_fits(int64_t blocks_x, int threads, int64_t y = 1, int64_t z = 1) {
+  return blocks_x >= 0 && blocks_x * threads <= 0xFFFFFFFFll && y >= 1 && y <= 65535 && z >= 1 &&
+         z <= 65535;
+}
+
 // Arguments of one attend launch: one layer, one scale step.
 struct AttendArgs {
   const void* q;          // [B][n][H][D]

@@ -939,6 +939,8 @@ hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s
   if (a.n_split < 1 || a.n_split > kMaxSplits ||
       (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
     return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 512) || !grid_fits((int64_t(a.B) * a.n * a.H + 7) / 8, 256))
+    return hipErrorInvalidConfiguration;
   if (a.n_split > 1) {
     hipLaunchKernelGGL((attend_q256_kernel<false, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();

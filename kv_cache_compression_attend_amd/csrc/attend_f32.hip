@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kThreads) void attend_f32_kernel(AttendArgs a) {
 
 template <int D>
 hipError_t launch_d(const AttendArgs& a, bool scas, hipStream_t s) {
+  if (!grid_fits(a.n_qtiles, kThreads, a.H, a.B)) return hipErrorInvalidConfiguration;
   const dim3 grid(a.n_qtiles, a.H, a.B);
   if (scas)
     hipLaunchKernelGGL((attend_f32_kernel<D, true>), grid, dim3(kThreads), 0, s, a);

@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   if (a.n_desc == 0) return hipSuccess;
+  if (!grid_fits(a.n_desc, kCopyThreads, a.B)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(gather_kernel, dim3(unsigned(a.n_desc), unsigned(a.B)), dim3(kCopyThreads), 0,
                      s, a);
   return hipGetLastError();
@@ -169,6 +170,7 @@ __global__ __launch_bounds__(kCopyThreads) void compact_rows_kernel(RowsArgs a) 
 hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s) {
   const int64_t blocks = int64_t(a.n_layers) * a.B * ((a.n + a.rows - 1) / a.rows);
   if (blocks == 0) return hipSuccess;
+  if (!grid_fits(blocks, kCopyThreads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(compact_rows_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
@@ -176,6 +178,7 @@ hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s) {
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
   if (blocks == 0) return hipSuccess;
+  if (!grid_fits(blocks, kCopyThreads)) return hipErrorInvalidConfiguration;
   if (int64_t(a.rows_per_block) * a.row_bytes > kCopyBlockBytes)
     hipLaunchKernelGGL(compact_kernel<2 * kCopyItems>, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, s, a);
   else

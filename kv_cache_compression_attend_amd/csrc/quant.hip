@@ -295,6 +295,8 @@ __global__ __launch_bounds__(kThreads) void quantize_codes_kernel(QuantArgs a) {
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
   if (a.n_desc == 0) return hipSuccess;
+  if (!grid_fits(int64_t(a.n_desc) * a.m * (a.nch > 1 ? a.nch : 1), kThreads, a.B, 2))
+    return hipErrorInvalidConfiguration;
   if (a.nch <= 1) {
     hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(a.n_desc * a.m), unsigned(a.B), 2u),
                        dim3(kThreads), 0, s, a);
@@ -310,6 +312,7 @@ hipError_t launch_quantize(const QuantArgs& a, hipStream_t s) {
 
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s) {
   if (a.n_items == 0) return hipSuccess;
+  if (!grid_fits(a.n_items, kThreads, a.B, 2)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(unpack_kernel, dim3(unsigned(a.n_items), unsigned(a.B), 2u), dim3(kThreads), 0,
                      s, a);
   return hipGetLastError();

@@ -67,6 +67,8 @@ def parse():
                     help="time the final-scale attend launch of the main workload on its random "
                          "inputs, with V zeroed, and with K and V zeroed (same instructions, less "
                          "operand toggling), then exit")
+    ap.add_argument("--cpu-passes", type=int, default=3,
+                    help="passes of the oracle over the sample (the whole layer takes ~4 s)")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
@@ -808,22 +810,24 @@ def cpu_baseline(args, wl, keep):
     from oracle.numerics import to_f64
 
     heads = list(range(min(args.cpu_heads, wl.heads)))
+    passes = max(1, args.cpu_passes)
     steps = [workloads.step_inputs(wl, 0, t) for t in range(wl.n_scales)]
     flops = 0.0
     start = time.perf_counter()
-    for t in range(wl.n_scales):
-        for h in heads:
-            kj, vj, src, lens = oatt.gather_keys([s.k for s in steps[: t + 1]],
-                                                 [s.v for s in steps[: t + 1]], keep[0, h], t, 0, h)
-            q = to_f64(steps[t].q[0, :, h, :], "bf16")
-            oatt.softmax_attention(q, to_f64(kj, "bf16"), to_f64(vj, "bf16"), wl.softmax_scale)
-            flops += 4.0 * wl.head_dim * q.shape[0] * kj.shape[0]
+    for _ in range(passes):
+        for t in range(wl.n_scales):
+            for h in heads:
+                kj, vj, src, lens = oatt.gather_keys([s.k for s in steps[: t + 1]],
+                                                     [s.v for s in steps[: t + 1]], keep[0, h], t, 0, h)
+                q = to_f64(steps[t].q[0, :, h, :], "bf16")
+                oatt.softmax_attention(q, to_f64(kj, "bf16"), to_f64(vj, "bf16"), wl.softmax_scale)
+                flops += 4.0 * wl.head_dim * q.shape[0] * kj.shape[0]
     secs = time.perf_counter() - start
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle", "seconds": round(secs, 2),
             "sample": f"full-cache layer, batch 1, all 13 scales of heads {heads[0]}..{heads[-1]} "
-                      f"({len(heads)} of {wl.heads}), fp64 NumPy"}
+                      f"({len(heads)} of {wl.heads}), fp64 NumPy, {passes} passes"}
 
 
 if __name__ == "__main__":

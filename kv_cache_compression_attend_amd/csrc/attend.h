@@ -35,8 +35,11 @@ struct AttendArgs {
   int B, H, n, K, step, n_qtiles;
   int rows;               // bf16: query rows per workgroup (128 or 256)
   int n_split;            // key-range splits per query tile (1: no split)
-  int append;             // 1: q-tile-0 workgroups also write this scale's kept
-                          // K/V rows into the cache (fused append)
+  int append;             // 1: the workgroups also write this scale's kept K/V
+                          // rows into the cache, key tile t by q-tile t mod
+                          // n_qtiles (fused append)
+  const int32_t* order;   // [H] heads heaviest first, or null; set only when B
+                          // is a multiple of kXcds (see attend_coords)
   float scale;            // softmax scale alpha
   float scale_log2;       // alpha * log2(e)
 };
@@ -49,6 +52,40 @@ __device__ __forceinline__ int xcd_logical(int i, int n) {
   const int q = n / kXcds, r = n % kXcds;
   const int x = i % kXcds, k = i / kXcds;
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
+// Work item of attend workgroup i: (batch entry, head, key-range split,
+// query tile).  Without a head order, logical index xcd_logical(i) in
+// (b, h, split, q-tile) order, q-tile fastest.  With one (the heads of a
+// pruned schedule hold different numbers of keys), die x takes batch entries
+// [x B/8, (x+1) B/8) and runs their work heaviest head first: (head rank,
+// batch entry, split, q-tile), so every die gets the same work and the
+// longest workgroups start first instead of forming the launch's tail.
+struct AttendItem {
+  int b, h, split, qt;
+};
+__device__ __forceinline__ AttendItem attend_coords(int i, int n, int B, int H, int n_split,
+                                                    int n_qtiles, const int32_t* order) {
+  AttendItem it;
+  if (order) {
+    const int x = i % kXcds, k = i / kXcds;
+    const int per_die = B / kXcds;
+    it.qt = k % n_qtiles;
+    int r = k / n_qtiles;
+    it.split = r % n_split;
+    r /= n_split;
+    it.b = x * per_die + r % per_die;
+    it.h = order[r / per_die];
+  } else {
+    const int wg = xcd_logical(i, n);
+    it.qt = wg % n_qtiles;
+    const int rest = wg / n_qtiles;
+    it.split = rest % n_split;
+    const int bh = rest / n_split;
+    it.h = bh % H;
+    it.b = bh / H;
+  }
+  return it;
 }
 
 // Query rows per workgroup (128 or 256) and key-range splits of one bf16

@@ -222,15 +222,13 @@ struct Head {
 
 __device__ __forceinline__ Head setup(const AttendArgs& a) {
   Head hd;
-  // Logical order: (b, h, split, q-tile), q-tile fastest, so the workgroups
-  // that read the same key range of a head are adjacent.
-  const int wg = xcd_logical(blockIdx.x, gridDim.x);
-  hd.qt = wg % a.n_qtiles;
-  const int rest = wg / a.n_qtiles;
-  hd.split = rest % a.n_split;
-  const int bh = rest / a.n_split;
-  hd.h = bh % a.H;
-  hd.b = bh / a.H;
+  // The workgroups that read the same key range of a head are adjacent on
+  // one die (q-tile fastest).
+  const AttendItem it = attend_coords(blockIdx.x, gridDim.x, a.B, a.H, a.n_split, a.n_qtiles, a.order);
+  hd.qt = it.qt;
+  hd.split = it.split;
+  hd.h = it.h;
+  hd.b = it.b;
   hd.n = a.n;
   const int64_t tok = int64_t(a.H) * D;
   hd.tokb = int(tok * 2);
@@ -934,7 +932,8 @@ AttendPlan attend_bf16_plan(int B, int H, int n, int max_keys, bool allow_split)
 hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
   const int rows = a.rows;
   const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
-  if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows)
+  if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows ||
+      (a.order && a.B % kXcds != 0))
     return hipErrorInvalidValue;
   if (a.n_split < 1 || a.n_split > kMaxSplits ||
       (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))

@@ -37,6 +37,13 @@ struct hk_ctx {
   int64_t* d_base = nullptr;
   int32_t* d_cap = nullptr;
   int32_t* d_lenb = nullptr;
+  // Heads of each (step, layer) heaviest first ([K][L][H]) and whether the
+  // bf16 attend launch of (step, layer) uses that order ([K][L]): only when
+  // its heads hold different numbers of keys and B is a multiple of the die
+  // count.
+  std::vector<int32_t> order;
+  std::vector<uint8_t> ordered;
+  int32_t* d_order = nullptr;
   hk::CopyDesc* d_desc = nullptr;
   hk::GatherDesc* d_gdesc = nullptr;
   hk::GatherRun* d_gruns = nullptr;
@@ -92,6 +99,8 @@ void free_tables(hk_ctx* c) {
   (void)hipFree(c->d_base);
   (void)hipFree(c->d_cap);
   (void)hipFree(c->d_lenb);
+  (void)hipFree(c->d_order);
+  c->d_order = nullptr;
   (void)hipFree(c->d_desc);
   (void)hipFree(c->d_gdesc);
   (void)hipFree(c->d_gruns);
@@ -188,6 +197,8 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.base = c->d_base + int64_t(layer) * c->H;
   a.cap = c->d_cap + int64_t(layer) * c->H;
   a.lenb = c->d_lenb + (int64_t(step) * c->L + layer) * c->H * c->K;
+  a.order = c->ordered[int64_t(step) * c->L + layer] ? c->d_order + (int64_t(step) * c->L + layer) * c->H
+                                                      : nullptr;
   a.partials = c->d_partials;
   a.ws_o = c->d_ws_o;
   a.ws_ml = c->d_ws_ml;
@@ -465,8 +476,23 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
     max_partials = std::max<int64_t>(max_partials, int64_t(B) * H * qt);
   }
 
+  // Dispatch order of each (step, layer): heads by keys held, most first
+  // (ties by index).
+  c->order.assign(int64_t(K) * heads, 0);
+  c->ordered.assign(int64_t(K) * L, 0);
+  for (int t = 0; t < K; ++t)
+    for (int l = 0; l < L; ++l) {
+      int32_t* ord = c->order.data() + (int64_t(t) * L + l) * H;
+      auto keys = [&](int h) { return lenb_at(t, int64_t(l) * H + h, t); };
+      for (int h = 0; h < H; ++h) ord[h] = h;
+      std::stable_sort(ord, ord + H, [&](int x, int y) { return keys(x) > keys(y); });
+      c->ordered[int64_t(t) * L + l] =
+          dtype == HK_DTYPE_BF16 && B % hk::kXcds == 0 && keys(ord[0]) != keys(ord[H - 1]);
+    }
+
   hipError_t e = hipGetDevice(&c->device);
   if (e == hipSuccess) e = upload(&c->d_base, c->base);
+  if (e == hipSuccess) e = upload(&c->d_order, c->order);
   std::vector<int32_t> cap32(c->cap.begin(), c->cap.end());
   if (e == hipSuccess) e = upload(&c->d_cap, cap32);
   if (e == hipSuccess) e = upload(&c->d_lenb, c->lenb);

@@ -477,6 +477,27 @@ def test_split_launch_with_empty_splits():
         run.ctx.close()
 
 
+def test_heads_heaviest_first_with_split_launch():
+    """Batch 8 with heads that hold different numbers of keys: each die runs
+    its batch entries' heads heaviest first (the per-step head order), also
+    in split launches and with empty splits; every (batch entry, head)
+    against the oracle, plain and fused."""
+    wl = _custom(92, "ordered-split", (1, 2, 3, 4, 6, 8, 12, 16, 24), heads=3, head_dim=128, batch=8,
+                 dtype="bf16")
+    keep = np.ones((1, wl.heads, wl.n_scales), dtype=np.uint8)
+    keep[:, :, -1] = 0
+    keep[0, 0, 1:] = 0          # head 0 keeps the sink only: the lightest, ranked last
+    keep[0, 1, 3:6] = 0         # head 1 drops a middle run
+    for fused in (False, True):
+        run = generate(wl, keep, [0], fused=fused)
+        rows, splits = run.ctx.attend_plan(wl.n_scales - 1)
+        assert rows == 256 and splits > 1, (rows, splits)
+        pairs = [(b, h) for b in range(wl.batch) for h in range(wl.heads)]
+        _compare_outputs(run, [0], rows_per_unit=64, bh=pairs)
+        check_cache(run, [0])
+        run.ctx.close()
+
+
 @pytest.mark.parametrize("mode", ["plain", "fused", "scas"])
 def test_rescale_on_peaked_scores(mode):
     """A softmax scale of 6 makes most queries' running max rise by more than

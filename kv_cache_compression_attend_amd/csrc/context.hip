@@ -695,12 +695,10 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
   }
   const int row_bytes = c->D * c->elem_bytes;
   const int rows_per_block = hk::kCopyBlockBytes / row_bytes;
-  if (last > first && 2 * (last - first) >= int64_t(nl) * c->H &&
-      c->tokens[step] < hk::kTokenBlockBytes / row_bytes) {
-    // A short scale that most heads store: per-head workgroups would each
-    // move little, so copy whole token blocks instead (contiguous reads,
-    // every head's rows written from one workgroup).  On long scales the
-    // per-head copy is faster (one contiguous write stream).
+  if (last > first && 2 * (last - first) >= int64_t(nl) * c->H && c->H <= hk::kRowsMaxHeads) {
+    // A scale that most heads store: copy whole token blocks (contiguous
+    // reads across the heads, every head's rows written from one workgroup),
+    // faster than per-head workgroups whose reads stride over the tokens.
     DeviceGuard g(c->device);
     if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
     hk::RowsArgs a{};

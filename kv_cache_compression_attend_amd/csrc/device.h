@@ -16,14 +16,15 @@ namespace hk {
 // the fastest plain contiguous copy and the faster compaction of launches
 // with few head runs; 8 per lane the faster one when a launch has at least
 // kCopyLargeMinBlocks blocks of the large size.  The in-place gather walks its
-// region in kGatherChunkBytes chunks, one pass each.  Scales shorter than
-// kTokenBlockBytes per head that most heads store are copied in token blocks.
+// region in kGatherChunkBytes chunks, one pass each.  Scales that most heads
+// store are copied in token blocks (contiguous reads across all heads) when a
+// layer has at most kRowsMaxHeads heads (their destinations sit in LDS).
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlockBytes = 16384;
 constexpr int kCopyBlockBytesLarge = 32768;
 constexpr int64_t kCopyLargeMinBlocks = 16384;
 constexpr int kGatherChunkBytes = 32768;
-constexpr int kTokenBlockBytes = 32768;
+constexpr int kRowsMaxHeads = 1024;
 
 // One kept (layer, head) segment of a completed scale, to be copied into the cache.
 struct CopyDesc {

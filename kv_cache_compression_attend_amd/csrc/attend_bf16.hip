@@ -11,8 +11,10 @@
 // Shared design:
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16: each lane owns one query column and 16 key
-//     rows per 32x32 block, so a query's max and sum stay in the lane (one
-//     exchange with the lane 32 apart per 32 keys).
+//     rows per 32x32 block, so a query's max and sum stay in the lane and
+//     the lane 32 apart that holds the query's other 16 keys (the two
+//     combine only when a block's exact max is needed, and once at the end
+//     for the denominator).
 //   * The key rows fed to the score product are permuted (bits 2 and 3 of the
 //     row index swapped) so that each lane's score registers already hold,
 //     for every 16-key step of the value product, the 8 consecutive keys the

@@ -337,10 +337,9 @@ __device__ __forceinline__ void write_split(const AttendArgs& a, const Head& hd,
 // accumulator of every source segment they fall in.  Source src < step
 // covers cache rows [lenb[src], lenb[src+1]); the current scale covers
 // [Lc, Ltot).  Bounds are wave-uniform scalar loads.
-template <typename Prob>
+template <int NT, typename Prob>
 __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, int hf,
-                                         const Prob& prob, float psum, int kblk,
-                                         float (&sc)[kMaxScales]) {
+                                         const Prob& prob, float psum, int kblk, float* sc) {
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
     if (src > a.step) break;
@@ -357,19 +356,22 @@ __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, in
           acc += (key >= lo && key < hi) ? prob(v) : 0.f;
         }
       }
-      sc[src] += acc;
+      sc[src * NT] += acc;
     }
   }
 }
 
-// Per-lane S-CAS accumulators: sc[src] is this query's unnormalised mass on
-// source src, relative to the running max.  Most 32-key blocks lie inside
-// one source segment, so their mass goes to one open accumulator (acc, for
-// source cur, whose keys end at hi); only a block that crosses a segment
-// boundary walks the segment list (scas_add) and moves the open segment on,
-// at most once per source per workgroup.
+// Per-lane S-CAS accumulators: sc[src * NT] (NT: the workgroup's threads) is this query's
+// unnormalised mass on source src, relative to the running max.  Most 32-key
+// blocks lie inside one source segment, so their mass goes to one open
+// accumulator in a register (acc, for source cur, whose keys end at hi); only
+// a block that crosses a segment boundary walks the segment list (scas_add)
+// and moves the open segment on, at most once per source per workgroup.  The
+// per-source sums are touched only there, on a rescale and at the end, so
+// they live in LDS (the lane's own column of a [kMaxScales][threads] array):
+// 16 registers fewer for the loop.
 struct ScasAcc {
-  float sc[kMaxScales];
+  float* sc;
   float acc;
   int cur, hi;
 };
@@ -386,37 +388,40 @@ __device__ __forceinline__ void scas_open(const AttendArgs& a, const Head& hd, S
   x.hi = seg_hi(a, hd, src);
 }
 
-__device__ __forceinline__ void scas_init(const AttendArgs& a, const Head& hd, ScasAcc& x) {
+template <int NT>
+__device__ __forceinline__ void scas_init(const AttendArgs& a, const Head& hd, ScasAcc& x,
+                                          float* lds) {
+  x.sc = lds + threadIdx.x;
 #pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) x.sc[s] = 0.f;
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s * NT] = 0.f;
   x.acc = 0.f;
   scas_open(a, hd, x, 0);
 }
 
+template <int NT>
 __device__ __forceinline__ void scas_flush(ScasAcc& x) {
-#pragma unroll
-  for (int s = 0; s < kMaxScales; ++s)
-    if (s == x.cur) x.sc[s] += x.acc;
+  x.sc[x.cur * NT] += x.acc;
   x.acc = 0.f;
 }
 
+template <int NT>
 __device__ __forceinline__ void scas_rescale(ScasAcc& x, float corr) {
 #pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) x.sc[s] *= corr;
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s * NT] *= corr;
   x.acc *= corr;
 }
 
 // Adds one 32-key block (keys kblk.., this lane's probabilities prob(v),
 // v = 0..15, summing to psum); blocks are added in key order.
-template <typename Prob>
+template <int NT, typename Prob>
 __device__ __forceinline__ void scas_block(const AttendArgs& a, const Head& hd, int hf,
                                            const Prob& prob, float psum, int kblk, ScasAcc& x) {
   if (kblk + 32 <= x.hi) {
     x.acc += psum;
     return;
   }
-  scas_flush(x);
-  scas_add(a, hd, hf, prob, psum, kblk, x.sc);
+  scas_flush<NT>(x);
+  scas_add<NT>(a, hd, hf, prob, psum, kblk, x.sc);
   scas_open(a, hd, x, kblk + 32);
 }
 
@@ -424,12 +429,12 @@ __device__ __forceinline__ void scas_block(const AttendArgs& a, const Head& hd, 
 // writes the workgroup's partial row.
 template <int WAVES>
 __device__ __forceinline__ void scas_reduce(const AttendArgs& a, const Head& hd, int qrow,
-                                            float inv, const float (&sc)[kMaxScales],
-                                            float* sRed) {
+                                            float inv, const ScasAcc& x, float* sRed) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
-    float m = (sc[src] + __shfl_xor(sc[src], 32)) * inv;
+    const float own = x.sc[src * WAVES * 64];
+    float m = (own + __shfl_xor(own, 32)) * inv;
     m = qrow < hd.n ? m : 0.f;
 #pragma unroll
     for (int off = 16; off >= 1; off >>= 1) m += __shfl_xor(m, off);
@@ -455,6 +460,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VSTR];
   __shared__ float sRed[SCAS ? 4 * kMaxScales : 1];
+  __shared__ float sScas[SCAS ? kMaxScales * 256 : 1];
 
   const Head hd = setup(a);
   const int tid = threadIdx.x;
@@ -471,7 +477,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   ScasAcc sa;
-  if constexpr (SCAS) scas_init(a, hd, sa);
+  if constexpr (SCAS) scas_init<256>(a, hd, sa, sScas);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -561,7 +567,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
         l_run *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db) oacc[db] *= corr;
-        if constexpr (SCAS) scas_rescale(sa, corr);
+        if constexpr (SCAS) scas_rescale<256>(sa, corr);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) ps[kb] = exp_pack<SCAS>(s[kb], c2, m_run, pb[kb]);
       }
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     l_run += ps[0] + ps[1];
     if constexpr (SCAS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) scas_block(a, hd, hf, ProbOf{s[kb], c2, m_run}, ps[kb], k0 + 32 * kb, sa);
+      for (int kb = 0; kb < 2; ++kb) scas_block<256>(a, hd, hf, ProbOf{s[kb], c2, m_run}, ps[kb], k0 + 32 * kb, sa);
     }
 
 #pragma unroll
@@ -587,8 +593,8 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
   store_out(a, hd, qrow, hf, oacc, inv);
   if constexpr (SCAS) {
-    scas_flush(sa);
-    scas_reduce<4>(a, hd, qrow, inv, sa.sc, sRed);
+    scas_flush<256>(sa);
+    scas_reduce<4>(a, hd, qrow, inv, sa, sRed);
   }
 }
 
@@ -647,6 +653,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[3][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3][D * VSTR];
   __shared__ float sRed[SCAS ? 8 * kMaxScales : 1];
+  __shared__ float sScas[SCAS ? kMaxScales * 512 : 1];
 
   const Head hd = setup(a);
   const int tid = threadIdx.x;
@@ -663,7 +670,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   ScasAcc sa;
-  if constexpr (SCAS) scas_init(a, hd, sa);
+  if constexpr (SCAS) scas_init<512>(a, hd, sa, sScas);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -732,7 +739,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
         l_run *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] *= corr;
-        if constexpr (SCAS) scas_rescale(sa, corr);
+        if constexpr (SCAS) scas_rescale<512>(sa, corr);
         psum = exp_pack<SCAS>(s, c2, m_run, p);
       }
     }
@@ -852,7 +859,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
                     std::true_type{}, s0, p0);
     settle(s0, p0, e0);
-    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
+    if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
     __syncthreads();
 
     // step b: unit (t, keys 32..63)
@@ -860,7 +867,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
                     std::integral_constant<bool, !LAST>{}, s1, p1);
     settle(s1, p1, e1);
-    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
+    if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
     bk = bn;
   };
   using T_ = std::true_type;
@@ -883,8 +890,8 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   const float inv = 1.f / l_tot;
   store_out(a, hd, qrow, hf, o, inv);
   if constexpr (SCAS) {
-    scas_flush(sa);
-    scas_reduce<8>(a, hd, qrow, inv, sa.sc, sRed);
+    scas_flush<512>(sa);
+    scas_reduce<8>(a, hd, qrow, inv, sa, sRed);
   }
 }
 

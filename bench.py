@@ -51,8 +51,11 @@ def attend_sources_sha() -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # One step of the default workload takes ~0.7 ms.  After the seconds of
+    # host-side set-up the GPU clock needs ~100 ms of work to ramp up: 5
+    # warmup passes left the timed average 4% slower than steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pruned", action="store_true",
                     help="skip the 32-layer 10%%-budget scales/s measurement")

@@ -903,7 +903,10 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 // per CU) takes kTile256, of a 128-query workgroup (two resident per CU)
 // kTile128; a workgroup's set-up (query load, first staging) adds kSetup*
 // tiles; a split launch adds the merge, kMerge plus kMergeRow per partial
-// output row.  Costs common to every choice (the launch) are left out.
+// output row.  Costs common to every choice (the launch) are left out.  A
+// split may be a single tile: timed inside whole generation passes, scale 5
+// of that layer at batch 1 (5 tiles, 16 workgroups) took 15.0-16.5 us in 5
+// one-tile splits against 20.6 us unsplit.
 namespace {
 constexpr double kTile256 = 1.80;
 constexpr double kTile128 = 2.00;
@@ -911,7 +914,7 @@ constexpr double kSetup256 = 0.17;
 constexpr double kSetup128 = 0.0;
 constexpr double kMerge = 3.15;
 constexpr double kMergeRow = 0.00024;
-constexpr int kMinTilesPerSplit = 2;
+constexpr int kMinTilesPerSplit = 1;
 }  // namespace
 
 AttendPlan attend_bf16_plan(int B, int H, int n, int max_keys, bool allow_split) {

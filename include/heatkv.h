@@ -37,11 +37,14 @@
  *     aligned.  hip_stream is a hipStream_t (NULL = the null stream).  Device
  *     work is enqueued asynchronously on that stream; faults during execution
  *     surface at the caller's next synchronisation.
- *   - The library allocates device memory only in hk_create (small tables and
- *     S-CAS partial sums) and frees it in hk_destroy; nothing allocates on the
- *     per-scale calls.
+ *   - The library allocates device memory only in hk_create* (small tables,
+ *     S-CAS partial sums, the key-range split workspace and, with 4-bit
+ *     storage, a one-layer bf16 scratch) and frees it in hk_destroy; nothing
+ *     allocates on the per-scale calls.
  *   - A context is not thread-safe: calls on one context must be serialised
- *     by the caller.
+ *     by the caller.  Its per-scale calls share that device workspace, so
+ *     calls on one context issued to different streams must not overlap on
+ *     the device (order the streams, or use one stream per context).
  */
 #ifndef HEATKV_H
 #define HEATKV_H

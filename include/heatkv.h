@@ -367,6 +367,19 @@ int hk_append_scale(hk_ctx* ctx, int layer_begin, int layer_end, int step, const
 int hk_attend_plan(const hk_ctx* ctx, int step, int with_scas, int32_t* rows_per_workgroup,
                    int32_t* splits);
 
+/* The plan hk_create picks for a bf16 launch, on the host and without a
+ * context: B batch entries, H heads, n queries per head (the scale's tokens)
+ * and at most max_keys keys per head (held rows plus n).  A cost model of
+ * launch rounds, key tiles per workgroup and the merge of split launches
+ * (constants measured on the MI355X) picks the query rows per workgroup
+ * (128 or 256) and the key-range splits (1 to 16, 256-row tiles only, at
+ * most one per 64-key tile; allow_split = 0, as for S-CAS launches, forces
+ * 1).
+ *   rows_per_workgroup, splits  host int32 (written)
+ * Errors: HK_EINVAL (a size < 1 or a null pointer). */
+int hk_plan_attend_bf16(int B, int H, int n, int max_keys, int allow_split,
+                        int32_t* rows_per_workgroup, int32_t* splits);
+
 /* Token slots per sequence held by the whole cache (all layers and heads)
  * once scale `step` has been appended: sum over kept s <= min(step, K-2). */
 int hk_retained_tokens(const hk_ctx* ctx, int step, int64_t* out);

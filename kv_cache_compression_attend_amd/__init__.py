@@ -27,7 +27,7 @@ import torch  # first: the library binds to the HIP runtime torch has loaded
 
 __all__ = ["HeatKVError", "build_schedule", "build_progressive_schedule", "build_scale_window_schedule",
            "cache_size_after_layer", "layout", "layout_expiry", "layout_int4", "scas_mean",
-           "ranking_stability", "Context", "library_path", "DTYPES"]
+           "ranking_stability", "plan_attend_bf16", "Context", "library_path", "DTYPES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libheatkv.so")
@@ -72,6 +72,7 @@ def _load():
         "hk_append_scale": ([P, I, I, I, P, P, I64, P], I),
         "hk_retained_tokens": ([P, I, P], I),
         "hk_attend_plan": ([P, I, I, P, P], I),
+        "hk_plan_attend_bf16": ([I, I, I, I, I, P, P], I),
         "hk_attend_append": ([P, I, I, P, P, P, P, F, P, P], I),
         "hk_attend_with_scas_sum": ([P, I, I, P, P, P, P, F, P, P], I),
         "hk_scas_mean": ([I, I, I, P, D, P], I),
@@ -119,6 +120,16 @@ def build_schedule(scas: np.ndarray, scale_tokens: Sequence[int], budget_frac: f
     _check(_lib.hk_build_schedule(L, H, K, _ptr(tok), _ptr(scas), float(budget_frac), int(n_sink),
                                   _ptr(keep), _ptr(ret), _ptr(npr)))
     return keep, ret, int(npr[0])
+
+
+def plan_attend_bf16(batch: int, heads: int, n: int, max_keys: int,
+                     allow_split: bool = True) -> Tuple[int, int]:
+    """(query rows per workgroup, key-range splits) of a bf16 launch (host only)."""
+    rows = np.zeros(1, dtype=np.int32)
+    splits = np.zeros(1, dtype=np.int32)
+    _check(_lib.hk_plan_attend_bf16(int(batch), int(heads), int(n), int(max_keys),
+                                    int(bool(allow_split)), _ptr(rows), _ptr(splits)))
+    return int(rows[0]), int(splits[0])
 
 
 def layout(scale_tokens: Sequence[int], keep: np.ndarray, batch: int,

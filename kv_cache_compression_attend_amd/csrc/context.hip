@@ -756,6 +756,17 @@ extern "C" int hk_retained_tokens(const hk_ctx* c, int step, int64_t* out) {
   return HK_OK;
 }
 
+extern "C" int hk_plan_attend_bf16(int B, int H, int n, int max_keys, int allow_split,
+                                   int32_t* rows_per_wg, int32_t* splits) {
+  if (!rows_per_wg || !splits) return fail(HK_EINVAL, "null argument");
+  if (B < 1 || H < 1 || n < 1 || max_keys < 1)
+    return fail(HK_EINVAL, "B, H, n and max_keys must be >= 1");
+  const hk::AttendPlan p = hk::attend_bf16_plan(B, H, n, max_keys, allow_split != 0);
+  *rows_per_wg = p.rows;
+  *splits = p.splits;
+  return HK_OK;
+}
+
 extern "C" int hk_attend_plan(const hk_ctx* c, int step, int with_scas, int32_t* rows_per_wg,
                               int32_t* splits) {
   if (!c || !rows_per_wg || !splits) return fail(HK_EINVAL, "null argument");

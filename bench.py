@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--pruned-steps", type=int, default=5)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
+    ap.add_argument("--summarize-pass", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-launch durations of one fused pass of the main line from a "
+                         "rocprofv3 kernel trace, then exit")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the average duration of the final-scale attend launch (the "
                          "largest-grid dispatches of the roofline kernel) from a rocprofv3 "
@@ -99,6 +102,46 @@ def summarize_trace(path):
     return {"kernel": ROOFLINE_KERNEL, "grid_threads": top, "dispatches": len(durs),
             "avg_ns": round(sum(durs) / len(durs), 1), "min_ns": min(durs), "max_ns": max(durs),
             "other_dispatches_of_kernel": len(rows) - len(durs)}
+
+
+def summarize_pass(path):
+    """Per-launch durations of one fused generation pass of the default
+    workload, from a rocprofv3 kernel trace of the main line: the dispatches
+    between consecutive final-scale launches (the roofline kernel's largest
+    grid) that contain no compaction kernel (those belong to the unfused
+    pass), median over the passes with the commonest launch sequence."""
+    import csv
+    import re
+    import statistics
+    seq = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            m = re.search(r"(\w+_kernel(?:<[\w, ]+>)?)", r["Kernel_Name"])
+            name = m.group(1) if m else r["Kernel_Name"]
+            seq.append((int(r["Start_Timestamp"]), name, grid,
+                        int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    seq.sort()
+    top = max((g for _, n, g, _ in seq if n == ROOFLINE_KERNEL), default=None)
+    if top is None:
+        raise SystemExit(f"no {ROOFLINE_KERNEL} dispatch in {path}")
+    ends = [i for i, (_, n, g, _) in enumerate(seq) if n == ROOFLINE_KERNEL and g == top]
+    passes = []
+    for a, b in zip(ends, ends[1:]):
+        part = seq[a + 1: b + 1]
+        if any("compact" in n for _, n, _, _ in part):
+            continue
+        passes.append(part)
+    if not passes:
+        raise SystemExit(f"no fused pass in {path}")
+    shapes = [tuple((n, g) for _, n, g, _ in p) for p in passes]
+    shape = max(set(shapes), key=shapes.count)
+    same = [p for p, s in zip(passes, shapes) if s == shape]
+    launches = [{"kernel": n, "grid_threads": g,
+                 "median_us": round(statistics.median(p[i][3] for p in same) / 1e3, 2)}
+                for i, (n, g) in enumerate(shape)]
+    return {"passes": len(same), "launches": launches,
+            "sum_median_us": round(sum(x["median_us"] for x in launches), 1)}
 
 
 def summarize_counters(paths):
@@ -230,6 +273,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
+        return
+    if args.summarize_pass:
+        print(json.dumps(summarize_pass(args.summarize_pass), indent=1))
         return
     if args.summarize_trace:
         print(json.dumps(summarize_trace(args.summarize_trace), indent=1))

@@ -129,3 +129,35 @@ def test_counter_summary_scales_by_the_copy_probe(bench, tmp_path):
     assert s["fetch_scale"] == pytest.approx(2.0) and s["write_scale"] == pytest.approx(1.0)
     assert s["bytes_per_launch"] == round((50000.0 * 2 + 16000.0) * 1024)
     assert s["kernel_sha256"] == bench.attend_sources_sha()
+
+
+def test_pass_summary_takes_the_fused_passes(bench, tmp_path):
+    """Launches between consecutive final-scale dispatches form one pass; a
+    pass that holds a compaction kernel (the unfused pass) is left out, and
+    each launch's duration is the median over the passes."""
+    hdr = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp",
+           "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    k = "void hk::(anonymous namespace)::" + bench.ROOFLINE_KERNEL + "(hk::AttendArgs)"
+    small = "void hk::(anonymous namespace)::attend_q128_kernel<false>(hk::AttendArgs)"
+    rows, t, did = [], 0, 0
+
+    def add(name, dur, grid):
+        nonlocal t, did
+        did += 1
+        rows.append(["KERNEL_DISPATCH", did, name, t, t + dur, grid, 1, 1])
+        t += dur + 100
+
+    add(k, 300000, 131072)
+    for small_ns, final_ns in ((5000, 320000), (7000, 330000), (6000, 340000)):
+        add(small, small_ns, 4096)
+        add(k, final_ns, 131072)
+    add("void hk::compact_rows_kernel(hk::RowsArgs)", 4000, 8192)   # an unfused pass
+    add(small, 90000, 4096)
+    add(k, 900000, 131072)
+    path = tmp_path / "trace.csv"
+    _write_csv(path, hdr, rows)
+    s = bench.summarize_pass(str(path))
+    assert s["passes"] == 3
+    assert [x["kernel"] for x in s["launches"]] == ["attend_q128_kernel<false>", bench.ROOFLINE_KERNEL]
+    assert [x["median_us"] for x in s["launches"]] == [6.0, 330.0]
+    assert s["sum_median_us"] == 336.0

@@ -82,3 +82,56 @@ def test_scas_mean_host():
     np.testing.assert_array_equal(hk.scas_mean(s, 7.0), (s / 7.0).astype(np.float32))
     with pytest.raises(hk.HeatKVError):
         hk.scas_mean(s, 0.0)
+
+
+def _stability_cases():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "stability_hand.json")) as f:
+        doc = json.load(f)
+    return doc, doc["cases"]
+
+
+def _pruned_set(keep):
+    L, H, K = keep.shape
+    return {(l, h, s) for l in range(L) for h in range(H) for s in range(K - 1) if not keep[l, h, s]}
+
+
+@pytest.mark.parametrize("case", range(3))
+def test_stability_hand_worked(case):
+    """Hand-worked pruned sets, Jaccard indices and rank correlations of two
+    different tables (tests/golden/stability_hand.json): the oracle and the
+    library both reproduce them."""
+    doc, cases = _stability_cases()
+    c = cases[case]
+    a = np.asarray(c["a"], dtype=np.float32)
+    b = np.asarray(c["b"], dtype=np.float32)
+    tok, beta, n_sink = doc["tokens"], doc["beta"], doc["n_sink"]
+    for tab, key in ((a, "pruned_a"), (b, "pruned_b")):
+        keep = osch.build_schedule(tab, tok, beta, n_sink)[0]
+        assert _pruned_set(keep) == {tuple(p) for p in c[key]}, (c["name"], key)
+        lib_keep = hk.build_schedule(tab, tok, beta, n_sink)[0]
+        assert _pruned_set(lib_keep) == {tuple(p) for p in c[key]}, (c["name"], key)
+    want_rho = np.array([math.nan if r is None else r for r in c["rho"]])
+    for rho, jac in (ocal.ranking_stability(a, b, tok, beta, n_sink),
+                     hk.ranking_stability(a, b, tok, beta, n_sink)):
+        assert abs(jac - c["jaccard"]) < 1e-12, (c["name"], jac)
+        np.testing.assert_array_equal(np.isnan(rho), np.isnan(want_rho))
+        np.testing.assert_allclose(rho[~np.isnan(rho)], want_rho[~np.isnan(want_rho)], rtol=0, atol=1e-12)
+
+
+def test_stability_jaccard_catches_planted_mistakes():
+    """The hand-worked Jaccard values separate the plausible slips: dividing
+    by |G_a| instead of the union, or counting the final scale's unstored
+    pairs as pruned."""
+    doc, cases = _stability_cases()
+    for c in cases:
+        ga = {tuple(p) for p in c["pruned_a"]}
+        gb = {tuple(p) for p in c["pruned_b"]}
+        fin = {(0, h, 3) for h in range(doc["H"])}
+        right = len(ga & gb) / len(ga | gb)
+        assert abs(right - c["jaccard"]) < 1e-12
+        if ga & gb and ga & gb != ga:
+            assert abs(len(ga & gb) / len(ga) - c["jaccard"]) > 0.1
+        wrong = len((ga | fin) & (gb | fin)) / len(ga | gb | fin)
+        assert abs(wrong - c["jaccard"]) > 0.1

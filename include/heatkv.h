@@ -261,7 +261,11 @@ int hk_destroy(hk_ctx* ctx);
 /* Start a new generation: every layer's cache is considered empty again. */
 int hk_reset(hk_ctx* ctx);
 
-/* Block-causal attention of scale `step` in `layer`.
+/* Block-causal attention of scale `step` in `layer` (HeatKV project page,
+ * Abstract and Method step 5: each scale attends to the key-value segments of
+ * earlier scales that survive pruning; Pith page of arXiv 2605.14877,
+ * Figure 2 caption: next-scale prediction conditions each scale on all
+ * earlier ones, and Figure 3 caption: tokens of a scale in raster order).
  *
  * For every (b, h) and query i of scale step:
  *   out[b][i][h][:] = softmax_j(softmax_scale * q[b][i][h][:] . key_j) value_j
@@ -271,7 +275,11 @@ int hk_reset(hk_ctx* ctx);
  * the products run on the matrix cores, probabilities are rounded to bf16 for
  * the value product, and out is rounded to bf16 (nearest even).
  * Order: requires that hk_append_scale has covered (layer, step-1) since the
- * last hk_reset (not needed for step 0).
+ * last hk_reset (not needed for step 0).  Under a schedule whose segments
+ * leave the cache after they were stored (hk_create_expiry), the append of a
+ * step that drops segments moves the survivors, so attending (layer, step)
+ * after the append of any step u >= step that drops segments of that layer
+ * returns HK_EORDER.
  * Errors: HK_EINVAL, HK_EORDER, HK_EHIP. */
 int hk_attend(hk_ctx* ctx, int layer, int step, const void* q, const void* k_cur,
               const void* v_cur, void* out, float softmax_scale, void* hip_stream);
@@ -381,7 +389,13 @@ int hk_plan_attend_bf16(int B, int H, int n, int max_keys, int allow_split,
                         int32_t* rows_per_workgroup, int32_t* splits);
 
 /* Token slots per sequence held by the whole cache (all layers and heads)
- * once scale `step` has been appended: sum over kept s <= min(step, K-2). */
+ * once scale `step` has been appended: the sum of n_s over the segments s <=
+ * min(step, K-2) held at the end of that step (HeatKV project page, Method
+ * steps 4-5: the cache must stay within the memory budget as scales are
+ * generated; Results, Table 1 excerpt, where the full cache factors over
+ * scales 0..K-2 only).  With a static keep-mask: the kept segments.
+ *   out   host int64 (written)
+ * Errors: HK_EINVAL (null, step outside [0, K)). */
 int hk_retained_tokens(const hk_ctx* ctx, int step, int64_t* out);
 
 #ifdef __cplusplus

@@ -171,12 +171,14 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   if (step > 0 && c->appended[layer] < step - 1)
     return fail(HK_EORDER, "attend(layer %d, step %d) needs scale %d appended first (last: %d)",
                 layer, step, step - 1, c->appended[layer]);
-  // Segments that leave the cache at this step are overwritten by the
-  // append: once that has run, this step's layout is gone.
+  // Segments that leave the cache at a step are overwritten by that step's
+  // append (the gather moves the survivors down): once the append of any
+  // step u >= step that drops segments has run, this step's layout is gone.
   const bool drops = c->drops[int64_t(step) * c->L + layer] != 0;
-  if (drops && c->appended[layer] >= step)
-    return fail(HK_EORDER, "attend(layer %d, step %d) after its append: the cache no longer holds "
-                "the segments this step reads", layer, step);
+  for (int u = step; u <= c->appended[layer]; ++u)
+    if (c->drops[int64_t(u) * c->L + layer])
+      return fail(HK_EORDER, "attend(layer %d, step %d) after the append of step %d, which moved "
+                  "the segments this step reads", layer, step, u);
   // Appending this scale as well needs the layer's cache to end at scale step-1.
   append = append && step <= c->K - 2;
   if (append && c->appended[layer] != step - 1)

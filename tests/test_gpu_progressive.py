@@ -228,6 +228,11 @@ def test_progressive_order_errors():
     with pytest.raises(hk.HeatKVError) as e:
         ctx.attend(0, 3, q, k, v, torch.empty_like(q), 1.0)   # layout of step 3 is gone
     assert e.value.status == hk.HK_EORDER
+    q2, k2, v2 = dev[2]
+    with pytest.raises(hk.HeatKVError) as e:
+        # step 2 itself drops nothing, but the append of step 3 moved its rows
+        ctx.attend(0, 2, q2, k2, v2, torch.empty_like(q2), 1.0)
+    assert e.value.status == hk.HK_EORDER
     torch.cuda.synchronize()
     ctx.close()
 

@@ -49,3 +49,15 @@ def test_dirichlet_table_rows():
     assert t.shape == (32, 16, 13, 13) and t.dtype == np.float32
     np.testing.assert_allclose(t.sum(axis=3), 1.0, atol=1e-5)
     assert np.all(np.triu(t[0, 0], 1) == 0)
+
+
+def test_leading_batch_entries_are_a_prefix_of_the_full_draw():
+    wl = workloads.get("c2")
+    full = workloads.step_inputs(wl, 3, 5)
+    for nb in (1, 3):
+        part = workloads.step_inputs(wl, 3, 5, batch=nb)
+        for a, b in ((part.q, full.q), (part.k, full.k), (part.v, full.v)):
+            np.testing.assert_array_equal(a, b[:nb])
+    wl3 = workloads.get("c3")
+    np.testing.assert_array_equal(workloads.step_inputs(wl3, 0, 6, batch=2).k,
+                                  workloads.step_inputs(wl3, 0, 6).k[:2])

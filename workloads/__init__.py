@@ -151,10 +151,12 @@ def step_inputs(wl: Workload, layer: int, step: int, seed: int = 0,
 
     Q, K ~ N(0,1) * qk_std, V ~ N(0,1).  Where the workload has key offsets,
     K = (Z + mu[h, step]) * qk_std.  ``batch`` (<= wl.batch) keeps only the
-    leading batch entries of the same draw.
+    leading batch entries of the same draw (batch is the leading axis, so they
+    are the first values of the generator's stream and only those are drawn).
     """
     n = wl.scale_tokens[step]
-    shape = (wl.batch, n, wl.heads, wl.head_dim)
+    nb = wl.batch if batch is None else min(int(batch), wl.batch)
+    shape = (nb, n, wl.heads, wl.head_dim)
     out = []
     mu = key_offsets(wl, seed)
     for tid in (TID_Q, TID_K, TID_V):
@@ -163,8 +165,6 @@ def step_inputs(wl: Workload, layer: int, step: int, seed: int = 0,
             z = z + mu[None, None, :, step, None]
         if tid in (TID_Q, TID_K):
             z = z * np.float32(wl.qk_std)
-        if batch is not None:
-            z = z[:batch]
         if wl.dtype == "bf16":
             out.append(round_to_bf16_bits(z))
         else:

@@ -398,6 +398,37 @@ int hk_plan_attend_bf16(int B, int H, int n, int max_keys, int allow_split,
  * Errors: HK_EINVAL (null, step outside [0, K)). */
 int hk_retained_tokens(const hk_ctx* ctx, int step, int64_t* out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): attention
+ * of one layer at scale `step`, as hk_attend_with_scas (scas_table != NULL)
+ * or hk_attend (scas_table == NULL), with no context and no allocation.
+ * The per-head tables and the S-CAS partial sums live in a device array of
+ * HK_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; every call on a GPU shares it, so calls that overlap on one
+ * GPU (other streams or threads) race.  The launch is never split over key
+ * ranges (the S-CAS launch plan), so outputs equal hk_attend_with_scas's bit
+ * for bit.
+ *   H <= HK_NOALLOC_MAX_HEADS heads, bf16, head_dim 128, B batch entries
+ *   scale_tokens   host int32 [K]
+ *   keep           host uint8 [H][K]: this layer's static keep-mask
+ *   k_cache, v_cache  device bf16: this layer's cache as hk_layout lays out
+ *                  one layer (head h at the sum over h' < h of B*cap[h']*128
+ *                  elements, [B][cap[h]][128]), holding every kept segment
+ *                  s < step (e.g. a context's cache + base[layer][0])
+ *   q, k_cur, v_cur, out  device bf16 [B][n_step][H][128]
+ *   scas_table     device float [H][K][K] or NULL; row `step` of every head
+ *                  is overwritten (entries s <= step)
+ * The current device must be the one holding the buffers.
+ * Errors: HK_EINVAL (sizes, nulls, alignment; H above the limit; B * H *
+ * query tiles whose S-CAS partial sums would not fit the array),
+ * HK_EUNSUPPORTED (K > HK_MAX_SCALES), HK_EHIP. */
+#define HK_NOALLOC_MAX_HEADS 32
+#define HK_NOALLOC_SCRATCH_BYTES (4 << 20)
+int hk_attend_noalloc(int H, int B, int K, const int32_t* scale_tokens, const uint8_t* keep,
+                      int step, const void* k_cache, const void* v_cache, const void* q,
+                      const void* k_cur, const void* v_cur, void* out, float softmax_scale,
+                      float* scas_table, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

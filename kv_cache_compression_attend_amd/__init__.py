@@ -27,7 +27,7 @@ import torch  # first: the library binds to the HIP runtime torch has loaded
 
 __all__ = ["HeatKVError", "build_schedule", "build_progressive_schedule", "build_scale_window_schedule",
            "cache_size_after_layer", "layout", "layout_expiry", "layout_int4", "scas_mean",
-           "ranking_stability", "plan_attend_bf16", "Context", "library_path", "DTYPES"]
+           "ranking_stability", "plan_attend_bf16", "attend_noalloc", "Context", "library_path", "DTYPES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libheatkv.so")
@@ -84,6 +84,7 @@ def _load():
         "hk_build_scale_window_schedule": ([I, I, I, P, I, I, I, P, I, P], I),
         "hk_layout_int4": ([I, I, I, P, P, I, I, I, P, P], I),
         "hk_create_int4": ([P, I, I, I, I, I, P, P, I, P, P], I),
+        "hk_attend_noalloc": ([I, I, I, P, P, I, P, P, P, P, P, P, F, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -266,6 +267,10 @@ def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+HK_NOALLOC_MAX_HEADS = 32
+HK_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
 class Context:

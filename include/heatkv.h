@@ -217,6 +217,46 @@ int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
                      const int32_t* scale_tokens, const uint8_t* expire, int dtype,
                      void* k_cache, void* v_cache);
 
+/* Pooled layout for an expiry-step schedule (hk_build_progressive_schedule's
+ * output, or any table with entries in [s, K-1]): instead of a region per
+ * head sized to that head's own peak, every head's rows live in one pool of
+ * rows per batch entry, and a segment that leaves the cache (Pith page of
+ * arXiv 2605.14877, Figure 4 caption: G_k is gone once scale k is done)
+ * gives its rows to segments stored later, so no stored row ever moves and
+ * the pool holds exactly the most token slots the cache holds at once.
+ * Rows are handed out in generation order -- for each scale k and each layer
+ * l: the segments of layer l that expire at k give back their rows, then the
+ * segments (l, h, k) that are stored take rows, lowest free rows first (the
+ * per-layer accounting of Algorithm 2, Appendix A of the same page) -- so
+ * pool_rows equals the largest per-layer cache size of
+ * hk_build_progressive_schedule's live_out.
+ *   pool_elems_out  host int64 (required): B * pool_rows * D, the elements of
+ *                   each buffer (K or V), laid out [B][pool_rows][D]
+ *   pool_rows_out   host int64 or NULL
+ *   seg_rows_out    host int32 [L][H][sum of n_s over s <= K-2] or NULL: for
+ *                   each head, segment after segment in scale order, the pool
+ *                   row of each of the segment's n_s rows, -1 for a segment
+ *                   that is never stored
+ * Errors: HK_EINVAL. */
+int hk_layout_pooled(int L, int H, int K, const int32_t* scale_tokens, const uint8_t* expire,
+                     int B, int D, int64_t* pool_elems_out, int64_t* pool_rows_out,
+                     int32_t* seg_rows_out);
+
+/* Create a context over a pooled cache (hk_layout_pooled) in the caller's
+ * k_pool / v_pool (bf16, head_dim 128, B * pool_rows * 128 elements each).
+ * Attention reads every held row through a per-(step, layer, head) map of
+ * pool rows; appends write the stored segments to their pool rows; dropped
+ * segments cost nothing (no gather).  Order rules, beyond hk_create's: a
+ * step is attended only before its own append (attend(l, t) needs the last
+ * appended step of layer l to be t-1), and append(l, t) needs every layer to
+ * have appended t-1 and the layers before l to have appended t, because the
+ * rows it takes may have been freed by those layers' segments (HK_EORDER
+ * otherwise).  hk_attend_append runs the attention and the append as two
+ * launches.
+ * Errors: as hk_create; HK_EUNSUPPORTED unless bf16 with D = 128. */
+int hk_create_pooled(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
+                     const uint8_t* expire, void* k_pool, void* v_pool);
+
 /* 4-bit storage of the retained cache (VAR-Q summary page, Key
  * contributions and Method: quantization groups indexed by (block, channel),
  * a block being one scale's segment, optionally cut into sub-blocks along

@@ -26,7 +26,7 @@ import numpy as np
 import torch  # first: the library binds to the HIP runtime torch has loaded
 
 __all__ = ["HeatKVError", "build_schedule", "build_progressive_schedule", "build_scale_window_schedule",
-           "cache_size_after_layer", "layout", "layout_expiry", "layout_int4", "scas_mean",
+           "cache_size_after_layer", "layout", "layout_expiry", "layout_pooled", "layout_int4", "scas_mean",
            "ranking_stability", "plan_attend_bf16", "attend_noalloc", "Context", "library_path", "DTYPES"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +85,8 @@ def _load():
         "hk_layout_int4": ([I, I, I, P, P, I, I, I, P, P], I),
         "hk_create_int4": ([P, I, I, I, I, I, P, P, I, P, P], I),
         "hk_attend_noalloc": ([I, I, I, P, P, I, P, P, P, P, P, P, F, P, P], I),
+        "hk_layout_pooled": ([I, I, I, P, P, I, I, P, P, P], I),
+        "hk_create_pooled": ([P, I, I, I, I, I, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -221,6 +223,26 @@ def layout_expiry(scale_tokens: Sequence[int], expire: np.ndarray, batch: int,
     return int(elems[0]), cap, base
 
 
+def layout_pooled(scale_tokens: Sequence[int], expire: np.ndarray, batch: int, head_dim: int,
+                  with_rows: bool = False):
+    """(elements of each pool buffer, pool rows per batch entry[, segment rows]) of the
+    pooled layout of an expiry-step schedule; segment rows [L][H][sum n_s, s <= K-2]
+    (int32, -1 for segments never stored) when with_rows."""
+    expire = np.ascontiguousarray(expire, dtype=np.uint8)
+    L, H, K = expire.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    elems = np.zeros(1, dtype=np.int64)
+    rows = np.zeros(1, dtype=np.int64)
+    seg = np.zeros((L, H, int(tok[: K - 1].sum())), dtype=np.int32) if with_rows else None
+    _check(_lib.hk_layout_pooled(L, H, K, _ptr(tok), _ptr(expire), int(batch), int(head_dim),
+                                 _ptr(elems), _ptr(rows), _ptr(seg) if with_rows else None))
+    if with_rows:
+        return int(elems[0]), int(rows[0]), seg
+    return int(elems[0]), int(rows[0])
+
+
 def layout_int4(scale_tokens: Sequence[int], keep: np.ndarray, batch: int, head_dim: int,
                 sub_blocks: int) -> Tuple[int, int]:
     """(bytes of each 4-bit store buffer, byte offset of its group parameters)."""
@@ -273,6 +295,51 @@ HK_NOALLOC_MAX_HEADS = 32
 HK_NOALLOC_SCRATCH_BYTES = 4 << 20
 
 
+def attend_noalloc(keep: np.ndarray, scale_tokens: Sequence[int], step: int,
+                   k_cache: Optional[torch.Tensor], v_cache: Optional[torch.Tensor], q: torch.Tensor,
+                   k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, softmax_scale: float,
+                   scas_table: Optional[torch.Tensor] = None, stream=None) -> None:
+    """hk_attend_noalloc: one layer's attention at scale ``step`` with no context
+    and no allocation.  keep [H][K] (this layer's static keep-mask); k_cache /
+    v_cache are views of that layer's cache (bf16, hk_layout order); q, k, v,
+    out bf16 [B][n_step][H][128]; scas_table float32 [H][K][K] or None."""
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    if keep.ndim != 2:
+        raise HeatKVError(HK_EINVAL, "keep must be [H][K]")
+    H, K = keep.shape
+    tok = np.ascontiguousarray(scale_tokens, dtype=np.int32)
+    if tok.shape != (K,):
+        raise HeatKVError(HK_EINVAL, "scale_tokens must have K entries")
+    if not (0 <= step < K):
+        raise HeatKVError(HK_EINVAL, f"step {step} out of range")
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise HeatKVError(HK_EINVAL, "q must be [B][n][H][128]")
+    B = q.shape[0]
+    want = (B, int(tok[step]), H, 128)
+    for x, nm in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        if (not isinstance(x, torch.Tensor) or tuple(x.shape) != want or x.dtype != torch.bfloat16
+                or not x.is_cuda or not x.is_contiguous()):
+            raise HeatKVError(HK_EINVAL, f"{nm} must be a contiguous bf16 device tensor {want}")
+    ptrs = []
+    for c in (k_cache, v_cache):
+        if c is None:
+            ptrs.append(None)
+        else:
+            if c.dtype != torch.bfloat16 or not c.is_cuda or not c.is_contiguous():
+                raise HeatKVError(HK_EINVAL, "caches must be contiguous bf16 device tensors")
+            ptrs.append(ctypes.c_void_p(c.data_ptr()))
+    tab = None
+    if scas_table is not None:
+        if (tuple(scas_table.shape) != (H, K, K) or scas_table.dtype != torch.float32
+                or not scas_table.is_cuda or not scas_table.is_contiguous()):
+            raise HeatKVError(HK_EINVAL, f"scas_table must be a contiguous float32 {(H, K, K)} device tensor")
+        tab = ctypes.c_void_p(scas_table.data_ptr())
+    _check(_lib.hk_attend_noalloc(int(H), int(B), int(K), _ptr(tok), _ptr(keep), int(step), ptrs[0],
+                                  ptrs[1], ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+                                  ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                  float(softmax_scale), tab, _stream(stream)))
+
+
 class Context:
     """A library context for one model (L layers x H heads) and one batch shape.
 
@@ -289,7 +356,7 @@ class Context:
                  scale_tokens: Sequence[int], keep: Optional[np.ndarray], dtype: torch.dtype,
                  k_cache: Optional[torch.Tensor] = None, v_cache: Optional[torch.Tensor] = None,
                  device=None, expire: Optional[np.ndarray] = None,
-                 sub_blocks: Optional[int] = None):
+                 sub_blocks: Optional[int] = None, pooled: bool = False):
         if dtype not in DTYPES:
             raise HeatKVError(HK_EUNSUPPORTED, f"dtype {dtype} not supported")
         self.sub_blocks = sub_blocks
@@ -308,7 +375,16 @@ class Context:
         self.expire = np.ascontiguousarray(expire, dtype=np.uint8) if expire is not None else None
         if np.asarray(sched).shape != (self.L, self.H, self.K):
             raise HeatKVError(HK_EINVAL, "the schedule must be [L][H][K]")
-        if expire is None:
+        self.pooled = bool(pooled)
+        self.pool_rows = None
+        if self.pooled:
+            if expire is None:
+                raise HeatKVError(HK_EINVAL, "a pooled cache takes a schedule of expiry steps")
+            self.cache_elems, self.pool_rows = layout_pooled(self.tokens, self.expire, self.B,
+                                                             self.D)
+            self.cap = np.full((self.L, self.H), self.pool_rows, dtype=np.int64)
+            self.base = np.zeros((self.L, self.H), dtype=np.int64)
+        elif expire is None:
             self.cache_elems, self.cap, self.base = layout(self.tokens, self.keep, self.B, self.D)
         else:
             self.cache_elems, self.cap, self.base = layout_expiry(self.tokens, self.expire, self.B,
@@ -330,10 +406,16 @@ class Context:
         create = _lib.hk_create if expire is None else _lib.hk_create_expiry
         table = self.keep if expire is None else self.expire
         with torch.cuda.device(self.device):
-            _check(create(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
-                          _ptr(tok), _ptr(table), DTYPES[dtype],
-                          ctypes.c_void_p(k_cache.data_ptr()),
-                          ctypes.c_void_p(v_cache.data_ptr())))
+            if self.pooled:
+                _check(_lib.hk_create_pooled(ctypes.byref(handle), self.L, self.H, self.D, self.B,
+                                             self.K, _ptr(tok), _ptr(table),
+                                             ctypes.c_void_p(k_cache.data_ptr()),
+                                             ctypes.c_void_p(v_cache.data_ptr())))
+            else:
+                _check(create(ctypes.byref(handle), self.L, self.H, self.D, self.B, self.K,
+                              _ptr(tok), _ptr(table), DTYPES[dtype],
+                              ctypes.c_void_p(k_cache.data_ptr()),
+                              ctypes.c_void_p(v_cache.data_ptr())))
         self._h = handle
 
     def _init_int4(self, layers, heads, head_dim, batch, scale_tokens, keep, dtype, k_store,

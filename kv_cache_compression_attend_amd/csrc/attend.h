@@ -42,6 +42,11 @@ struct AttendArgs {
                           // is a multiple of kXcds (see attend_coords)
   float scale;            // softmax scale alpha
   float scale_log2;       // alpha * log2(e)
+  // Pooled cache (null otherwise): every head's rows sit in one pool per
+  // batch entry (base 0, cap = pool rows); cache row r of head h at this
+  // step is pool row map[mapoff[h] + r].  No fused append with a pool.
+  const int32_t* map;
+  const int64_t* mapoff;  // [H]
 };
 
 // Workgroups are handed to the 8 dies round-robin (workgroup i runs on die

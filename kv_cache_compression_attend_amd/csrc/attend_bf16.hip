@@ -21,8 +21,9 @@
 //     B operand of O^T = V^T P^T needs: probabilities go from the score
 //     registers straight into the value product.
 //   * K tiles are staged row-major in LDS; V tiles are transposed on the way
-//     in (4 keys x 8 dims per lane, repacked in registers) so the A operand
-//     of the value product is one 16-byte LDS read.  Row strides are padded
+//     in (4 keys x 8 dims per lane, repacked in registers with byte
+//     permutes) so the A operand of the value product is one 16-byte LDS
+//     read.  Row strides are padded
 //     so the operand reads are free of bank conflicts.
 //   * Global loads are buffer loads from per-tile scalar descriptors whose
 //     size ends at the last valid row, so rows past the end read as zero and
@@ -39,6 +40,17 @@
 //     wave take the block's exact max and, if it must, rescale and take the
 //     exponentials again.  The common block thus spends nothing on its max
 //     or on the cross-lane exchange the max needs.
+//   * Without S-CAS and for alpha * log2 e <= 2, Q is multiplied by
+//     alpha * log2 e once per workgroup (and rounded to bf16), so the score
+//     products come out in base-2 units,
+//     and the 256-query tiling runs the middle key tiles of a wave without
+//     any running max while its scores stay within +-64 of zero (2^64 and
+//     2^-64 are far inside fp32 and bf16 range): the exponentials then take
+//     the accumulators as they are, with no scaling or subtraction.  A block
+//     whose probabilities sum above 2^64 raises the running max at once and
+//     the wave continues in the general form.  (With S-CAS the scores keep
+//     the exact bf16 Q: the per-source mass of a single query is compared
+//     to 1e-4.)
 //   * Without S-CAS the softmax denominator is summed from the same bf16
 //     probabilities the value product uses (v_dot2 against ones: half the
 //     adds).  With S-CAS it is summed in fp32 together with per-source
@@ -91,6 +103,15 @@ constexpr int kRowBytes = D * 2;
 constexpr int kMaxSplits = 16;  // key-range splits per head in one launch
 constexpr float kRescaleSlack = 8.f;  // log2 units
 constexpr float kSumTrigger = 128.f;   // 2^(kRescaleSlack - 1)
+constexpr float kFastRange = 64.f;     // log2 units: |first block max| allowed in fast mode
+constexpr float kFastTrigger = 1.8446744e19f;  // 2^kFastRange
+// Largest alpha * log2 e for which Q is pre-scaled.  Rounding alpha * log2 e
+// * q to bf16 moves each term of a score's dot product by up to 2^-8 of
+// itself, so the score error grows with the scale: up to 2 (alpha ~1.4, the
+// workloads' alpha = 1) it perturbs a probability about as much as its own
+// bf16 rounding before the value product; a softmax scale of 6 measured
+// twice the bf16 parity bar, so larger scales keep the exact Q.
+constexpr float kPreMaxScale = 2.f;
 constexpr unsigned kOutOfRange = 0x80000000u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
@@ -136,19 +157,35 @@ __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, unsigned off) {
 // Where the keys (or values) of one (batch, head) live: cache rows [0, Lc),
 // then the current scale's rows; Ltot keys in all.
 struct KeySource {
-  const char* cache;  // row r at cache + r * kRowBytes
+  const char* cache;  // row r at cache + r * kRowBytes (pooled: at cache + map[r] * kRowBytes)
   const char* cur;    // row r at cur + r * tokb
   int Lc, Ltot, n, tokb;
+  const int32_t* map;  // pooled caches: pool row of each held row, else null
+  int pool_bytes;      // pooled caches: bytes of the batch entry's pool
 };
 
 // Four 16-byte vectors of the 64-row tile starting at key k0: rows
 // r0 + rstep * i (i = 0..3), 16-byte chunk c.  Rows past the end read 0.
+// PAGED: cache rows are found through the map (one 4-byte load per row,
+// then the row itself).
+template <bool PAGED>
 __device__ __forceinline__ void load_rows(const KeySource& s, int k0, int r0, int rstep, int c,
                                           u32x4 (&reg)[4]) {
   if (k0 + BN <= s.Lc) {  // all rows in the cache
-    const auto r = rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
+    if constexpr (PAGED) {
+      const auto rm = rsrc(s.map + k0, BN * 4);
+      const auto rp = rsrc(s.cache, s.pool_bytes);
+      unsigned pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) reg[i] = bload(r, unsigned(r0 + rstep * i) * kRowBytes + 16u * c);
+      for (int i = 0; i < 4; ++i)
+        pr[i] = __builtin_amdgcn_raw_buffer_load_b32(rm, (r0 + rstep * i) * 4, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) reg[i] = bload(rp, pr[i] * unsigned(kRowBytes) + 16u * c);
+    } else {
+      const auto r = rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) reg[i] = bload(r, unsigned(r0 + rstep * i) * kRowBytes + 16u * c);
+    }
   } else if (k0 >= s.Lc) {  // all rows in the current scale
     const int64_t q0 = k0 - s.Lc;
     const auto r = rsrc(s.cur + q0 * s.tokb, int64_t(s.n - q0 - 1) * s.tokb + kRowBytes);
@@ -156,21 +193,38 @@ __device__ __forceinline__ void load_rows(const KeySource& s, int k0, int r0, in
     for (int i = 0; i < 4; ++i) reg[i] = bload(r, unsigned(r0 + rstep * i) * s.tokb + 16u * c);
   } else {  // junction: rows below split from the cache, the rest from the current scale
     const int split = s.Lc - k0;
-    const auto rc = rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
     const auto ru = rsrc(s.cur - int64_t(split) * s.tokb, int64_t(split + s.n - 1) * s.tokb + kRowBytes);
+    if constexpr (PAGED) {
+      const auto rm = rsrc(s.map + k0, split * 4);
+      const auto rp = rsrc(s.cache, s.pool_bytes);
+      unsigned pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = r0 + rstep * i;
-      const unsigned oc = row < split ? unsigned(row) * kRowBytes + 16u * c : kOutOfRange;
-      const unsigned ou = row >= split ? unsigned(row) * s.tokb + 16u * c : kOutOfRange;
-      reg[i] = bload(rc, oc) | bload(ru, ou);
+      for (int i = 0; i < 4; ++i)
+        pr[i] = __builtin_amdgcn_raw_buffer_load_b32(rm, (r0 + rstep * i) * 4, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + rstep * i;
+        const unsigned oc = row < split ? pr[i] * unsigned(kRowBytes) + 16u * c : kOutOfRange;
+        const unsigned ou = row >= split ? unsigned(row) * s.tokb + 16u * c : kOutOfRange;
+        reg[i] = bload(rp, oc) | bload(ru, ou);
+      }
+    } else {
+      const auto rc = rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + rstep * i;
+        const unsigned oc = row < split ? unsigned(row) * kRowBytes + 16u * c : kOutOfRange;
+        const unsigned ou = row >= split ? unsigned(row) * s.tokb + 16u * c : kOutOfRange;
+        reg[i] = bload(rc, oc) | bload(ru, ou);
+      }
     }
   }
 }
 
 // K staging over 256 lanes: lane l holds chunk l & 15 of rows (l >> 4) + 16 i.
+template <bool PAGED>
 __device__ __forceinline__ void load_k(const KeySource& s, int k0, int l, u32x4 (&reg)[4]) {
-  load_rows(s, k0, l >> 4, 16, l & 15, reg);
+  load_rows<PAGED>(s, k0, l >> 4, 16, l & 15, reg);
 }
 __device__ __forceinline__ void store_k(uint16_t* sK, int l, const u32x4 (&reg)[4]) {
 #pragma unroll
@@ -180,8 +234,9 @@ __device__ __forceinline__ void store_k(uint16_t* sK, int l, const u32x4 (&reg)[
 
 // V staging over 256 lanes: lane l holds chunk l >> 4 of rows 4 (l & 15) + r,
 // written transposed (dims x keys).
+template <bool PAGED>
 __device__ __forceinline__ void load_v(const KeySource& s, int k0, int l, u32x4 (&reg)[4]) {
-  load_rows(s, k0, 4 * (l & 15), 1, l >> 4, reg);
+  load_rows<PAGED>(s, k0, 4 * (l & 15), 1, l >> 4, reg);
 }
 __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[4]) {
   const int g = l & 15, c = l >> 4;
@@ -189,10 +244,10 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
   for (int w = 0; w < 4; ++w) {
     const uint32_t a0 = reg[0][w], a1 = reg[1][w], a2 = reg[2][w], a3 = reg[3][w];
     uint2 even, odd;
-    even.x = (a0 & 0xFFFFu) | (a1 << 16);
-    even.y = (a2 & 0xFFFFu) | (a3 << 16);
-    odd.x = (a0 >> 16) | (a1 & 0xFFFF0000u);
-    odd.y = (a2 >> 16) | (a3 & 0xFFFF0000u);
+    even.x = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+    even.y = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+    odd.x = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    odd.y = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
     const int d = 8 * c + 2 * w;
     *reinterpret_cast<uint2*>(&sV[d * VSTR + 4 * g]) = even;
     *reinterpret_cast<uint2*>(&sV[(d + 1) * VSTR + 4 * g]) = odd;
@@ -202,8 +257,10 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
 // Fused append: the 16-byte chunks held in reg (rows r0 + rstep * i, chunk c
 // of the tile at key k0) whose key falls in the current scale are written to
 // the same key's row of the cache, where the scale's segment starts at row Lc.
+template <bool PAGED>
 __device__ __forceinline__ void append_rows(const KeySource& s, char* cache, int k0, int r0, int rstep,
                                             int c, const u32x4 (&reg)[4]) {
+  if constexpr (PAGED) return;  // pooled caches are appended by their own kernel
   if (k0 + BN <= s.Lc) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -240,10 +297,14 @@ __device__ __forceinline__ Head setup(const AttendArgs& a) {
   hd.Lc = hd.lenb[a.step];
   hd.Ltot = hd.Lc + hd.n;
   const int64_t curoff = (int64_t(hd.b) * hd.n * tok + hd.h * D) * 2;
+  // A pooled cache: every head's rows sit in the batch entry's pool of cap
+  // rows (base 0), found through this step's map of the head.
+  const int32_t* map = a.map ? a.map + a.mapoff[hd.h] : nullptr;
+  const int pool_bytes = a.map ? cap * kRowBytes : 0;
   hd.ks = KeySource{static_cast<const char*>(a.kcache) + hb, static_cast<const char*>(a.kcur) + curoff,
-                    hd.Lc, hd.Ltot, hd.n, hd.tokb};
+                    hd.Lc, hd.Ltot, hd.n, hd.tokb, map, pool_bytes};
   hd.vs = KeySource{static_cast<const char*>(a.vcache) + hb, static_cast<const char*>(a.vcur) + curoff,
-                    hd.Lc, hd.Ltot, hd.n, hd.tokb};
+                    hd.Lc, hd.Ltot, hd.n, hd.tokb, map, pool_bytes};
   hd.q = static_cast<const char*>(a.q) + curoff;
   // Every workgroup of a (b, h, split) stages all of its key tiles; the
   // append of tile t falls to the one with q-tile t mod n_qtiles, so the
@@ -455,7 +516,7 @@ __device__ __forceinline__ void scas_reduce(const AttendArgs& a, const Head& hd,
 // ---------------------------------------------------------------------------
 // With S-CAS the per-lane source accumulators do not fit beside the rest in
 // 256 registers, so that variant runs one wave per SIMD instead of spilling.
-template <bool SCAS>
+template <bool SCAS, bool PAGED>
 __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VSTR];
@@ -491,21 +552,21 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   int next_append = first_append_tile(a, hd, t_lo);
   auto append_tile = [&](int t) {
     if (hd.append && t == next_append) {
-      append_rows(hd.ks, kc_w, t * BN, tid >> 4, 16, tid & 15, kreg);
-      append_rows(hd.vs, vc_w, t * BN, 4 * (tid & 15), 1, tid >> 4, vreg);
+      append_rows<PAGED>(hd.ks, kc_w, t * BN, tid >> 4, 16, tid & 15, kreg);
+      append_rows<PAGED>(hd.vs, vc_w, t * BN, 4 * (tid & 15), 1, tid >> 4, vreg);
       next_append += a.n_qtiles;
     }
   };
 
   if (t_lo < t_hi) {
-    load_k(hd.ks, t_lo * BN, tid, kreg);
-    load_v(hd.vs, t_lo * BN, tid, vreg);
+    load_k<PAGED>(hd.ks, t_lo * BN, tid, kreg);
+    load_v<PAGED>(hd.vs, t_lo * BN, tid, vreg);
     store_k(sK[0], tid, kreg);
     store_v(sV[0], tid, vreg);
     append_tile(t_lo);
     if (t_lo + 1 < t_hi) {
-      load_k(hd.ks, (t_lo + 1) * BN, tid, kreg);
-      load_v(hd.vs, (t_lo + 1) * BN, tid, vreg);
+      load_k<PAGED>(hd.ks, (t_lo + 1) * BN, tid, kreg);
+      load_v<PAGED>(hd.vs, (t_lo + 1) * BN, tid, vreg);
     }
   }
   __syncthreads();
@@ -519,8 +580,8 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
       append_tile(it + 1);
     }
     if (it + 2 < t_hi) {
-      load_k(hd.ks, k0 + 2 * BN, tid, kreg);
-      load_v(hd.vs, k0 + 2 * BN, tid, vreg);
+      load_k<PAGED>(hd.ks, k0 + 2 * BN, tid, kreg);
+      load_v<PAGED>(hd.vs, k0 + 2 * BN, tid, vreg);
     }
 
     // Scores S^T for two 32-key blocks.
@@ -648,7 +709,9 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // ---------------------------------------------------------------------------
 // SPLIT: the launch splits each head's key range (a.n_split > 1); a separate
 // instantiation, so the unsplit kernel carries no split code.
-template <bool SCAS, bool SPLIT>
+// PRE (never with S-CAS): Q scaled by alpha * log2 e and rounded to bf16,
+// with the fast mode; only for alpha * log2 e <= kPreMaxScale.
+template <bool SCAS, bool SPLIT, bool PAGED, bool PRE>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[3][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[3][D * VSTR];
@@ -664,6 +727,25 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   const int qrow = hd.qt * 256 + wave * 32 + j;
   Vec16 qf[8];
   load_q(hd, qrow, hf, qf);
+  // Without S-CAS, Q is scaled by alpha * log2 e once (rounded to bf16), so
+  // the score products come out in base-2 units.  While a wave's scores stay
+  // within +-kFastRange of zero no running max is subtracted at all (fast
+  // mode): the exponentials take the accumulators as they are.  A block whose
+  // probabilities sum above 2^kFastRange (or a first block outside the range)
+  // moves the wave to the running-max form at the end of its key tile.
+  static_assert(!(PRE && SCAS), "S-CAS keeps the exact bf16 Q");
+  if constexpr (PRE) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t x = qf[kk].w[w];
+        const float lo = __builtin_bit_cast(float, x << 16) * a.scale_log2;
+        const float hi = __builtin_bit_cast(float, x & 0xFFFF0000u) * a.scale_log2;
+        qf[kk].w[w] = pack_bf16x2(lo, hi);
+      }
+  }
+  bool fast = false;
 
   f32x16 o[4];
 #pragma unroll
@@ -674,7 +756,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
-  const float c2 = a.scale_log2;
+  const float c2 = PRE ? 1.f : a.scale_log2;
   // Key tiles [t_lo, t_hi) of this workgroup's split.
   const int ntiles_all = (Ltot + BN - 1) / BN;
   const int per_split = SPLIT ? (ntiles_all + a.n_split - 1) / a.n_split : ntiles_all;
@@ -725,6 +807,33 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // output accumulators (which already hold the previous unit's value
   // product), the denominator and the S-CAS sums are rescaled, and the unit's
   // exponentials are taken again.
+  // Fast mode (scores relative to m_run, which is 0 until the wave leaves
+  // the mode): a block sum above 2^kFastRange raises m_run by the block's
+  // max (where positive), rescales, and ends fast mode after this tile; the
+  // next unit's scores, when this tile still takes their exponentials
+  // (shift_next), are moved to the new reference.
+  auto settle_fast = [&](const f32x16& s, Vec16 (&p)[2], float& psum, f32x16& snext,
+                         bool shift_next) {
+    if (__builtin_expect(__any(!(psum <= kFastTrigger)), 0)) {
+      float t = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) t = fmaxf(t, s[v]);
+      t = fmaxf(t, __shfl_xor(t, 32));
+      const float d = fmaxf(t, 0.f);
+      m_run += d;
+      const float corr = __builtin_amdgcn_exp2f(-d);
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] *= corr;
+      psum = exp_pack<SCAS>(s, 1.f, d, p);
+      if (shift_next) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) snext[v] -= d;
+      }
+      fast = false;
+    }
+    l_run += psum;
+  };
   auto settle = [&](const f32x16& s, Vec16 (&p)[2], float& psum) {
     if (__builtin_expect(__any(!(psum <= kSumTrigger)), 0)) {
       float t = -INFINITY;
@@ -751,9 +860,10 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // current unit's exponentials, packing and denominator.
   auto step = [&](const uint16_t* Vt, int kbv, const Vec16 (&pprev)[2], auto do_pv_c,
                   const uint16_t* Kt, int kbk, f32x16& snext, auto do_qk_c, f32x16& s,
-                  Vec16 (&p)[2]) {
+                  Vec16 (&p)[2], auto fast_c) {
     constexpr bool DO_PV = decltype(do_pv_c)::value;
     constexpr bool DO_QK = decltype(do_qk_c)::value;
+    constexpr bool FAST = decltype(fast_c)::value;
     const uint16_t* kp = Kt + (32 * kbk + kb_row) * KSTR + 8 * hf;
     auto frag = [&](int i) {
       Vec16 f;
@@ -785,7 +895,8 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      e[i & 1] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_run));
+      if constexpr (FAST) e[i & 1] = __builtin_amdgcn_exp2f(s[i]);
+      else e[i & 1] = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -m_run));
       if (i & 1) {
         const int half = i >> 3, w = (i & 7) >> 1;
         p[half].w[w] = pack_bf16x2(e[0], e[1]);
@@ -818,24 +929,37 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // stays in a scalar register.
   int next_append = first_append_tile(a, hd, t_lo);
   if (kstager) {
-    load_k(hd.ks, k_lo, stid, reg);
+    load_k<PAGED>(hd.ks, k_lo, stid, reg);
     store_k(sK[0], stid, reg);
-    if (hd.append && t_lo == next_append) append_rows(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
-    if (t_lo + 1 < t_hi) load_k(hd.ks, k_lo + BN, stid, reg);
+    if (hd.append && t_lo == next_append) append_rows<PAGED>(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
+    if (t_lo + 1 < t_hi) load_k<PAGED>(hd.ks, k_lo + BN, stid, reg);
   } else {
-    load_v(hd.vs, k_lo, stid, reg);
+    load_v<PAGED>(hd.vs, k_lo, stid, reg);
   }
   __syncthreads();
   qk(sK[0], 0, s0);
+  if constexpr (PRE) {
+    // The first unit (it always holds a valid key) sets the reference: 0
+    // when its exact max lies within +-kFastRange for every query of the
+    // wave (the first tile's probabilities are then already those of fast
+    // mode, none pending needs converting), else that max.
+    mask_tail(s0, k_lo);
+    float t = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t = fmaxf(t, s0[v]);
+    t = fmaxf(t, __shfl_xor(t, 32));
+    m_run = __all(t >= -kFastRange && t <= kFastRange) ? 0.f : t;
+  }
 
   // One 64-key tile; FIRST (the split's first tile) drops the value product
   // of the absent previous unit, LAST (its last) the score product of the
   // absent next tile and enables the tail mask, which only the head's final
   // tile needs.
   int bk = 0;  // LDS buffer of K(t) and of V(t)
-  auto tile = [&](int t, auto first_c, auto last_c) {
+  auto tile = [&](int t, auto first_c, auto last_c, auto fast_c) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
+    constexpr bool FAST = decltype(fast_c)::value;
     const int k0 = t * BN;
     const int bn = bk == 2 ? 0 : bk + 1;
     const int bp = bk == 0 ? 2 : bk - 1;
@@ -845,39 +969,49 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if (kstager) {
       if constexpr (!LAST) {
         store_k(sK[bn], stid, reg);
-        if (append_k) append_rows(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
+        if (append_k) append_rows<PAGED>(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
       }
-      if (t + 2 < t_hi) load_k(hd.ks, k0 + 2 * BN, stid, reg);
+      if (t + 2 < t_hi) load_k<PAGED>(hd.ks, k0 + 2 * BN, stid, reg);
     } else {
       store_v(sV[bk], stid, reg);
-      if (append_v) append_rows(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
-      if constexpr (!LAST) load_v(hd.vs, k0 + BN, stid, reg);
+      if (append_v) append_rows<PAGED>(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
+      if constexpr (!LAST) load_v<PAGED>(hd.vs, k0 + BN, stid, reg);
     }
 
     // step a: unit (t, keys 0..31)
     if constexpr (LAST) mask_tail(s0, k0);
     float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
-                    std::true_type{}, s0, p0);
-    settle(s0, p0, e0);
+                    std::true_type{}, s0, p0, fast_c);
+    if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
+    else settle(s0, p0, e0);
     if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
     __syncthreads();
 
     // step b: unit (t, keys 32..63)
     if constexpr (LAST) mask_tail(s1, k0 + 32);
     float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
-                    std::integral_constant<bool, !LAST>{}, s1, p1);
-    settle(s1, p1, e1);
+                    std::integral_constant<bool, !LAST>{}, s1, p1, fast_c);
+    if constexpr (FAST) settle_fast(s1, p1, e1, s0, false);
+    else settle(s1, p1, e1);
     if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
     bk = bn;
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
   if (t_hi - t_lo == 1) {
-    tile(t_lo, T_{}, T_{});
+    tile(t_lo, T_{}, T_{}, F_{});
   } else {
-    tile(t_lo, T_{}, F_{});
-    for (int t = t_lo + 1; t + 1 < t_hi; ++t) tile(t, F_{}, F_{});
-    tile(t_hi - 1, F_{}, T_{});
+    tile(t_lo, T_{}, F_{}, F_{});
+    int t = t_lo + 1;
+    if constexpr (PRE) {
+      // Where the reference is still 0 after the first tile for every query
+      // of the wave, the middle tiles run in fast mode until a block leaves
+      // the range.
+      fast = __all(m_run == 0.f);
+      for (; fast && t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, T_{});
+    }
+    for (; t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, F_{});
+    tile(t_hi - 1, F_{}, T_{}, F_{});
   }
   pv(sV[bk == 0 ? 2 : bk - 1], 1, p1);
 
@@ -941,19 +1075,17 @@ AttendPlan attend_bf16_plan(int B, int H, int n, int max_keys, bool allow_split)
   return best;
 }
 
-hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
-  const int rows = a.rows;
+namespace {
+
+template <bool PAGED>
+hipError_t launch_attend(const AttendArgs& a, bool scas, hipStream_t s) {
   const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
-  if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows ||
-      (a.order && a.B % kXcds != 0))
-    return hipErrorInvalidValue;
-  if (a.n_split < 1 || a.n_split > kMaxSplits ||
-      (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
-    return hipErrorInvalidValue;
-  if (!grid_fits(blocks, 512) || !grid_fits((int64_t(a.B) * a.n * a.H + 7) / 8, 256))
-    return hipErrorInvalidConfiguration;
+  const bool pre = a.scale_log2 <= kPreMaxScale;
   if (a.n_split > 1) {
-    hipLaunchKernelGGL((attend_q256_kernel<false, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
+    if (pre)
+      hipLaunchKernelGGL((attend_q256_kernel<false, true, PAGED, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((attend_q256_kernel<false, true, PAGED, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t out_rows = int64_t(a.B) * a.n * a.H;
@@ -968,18 +1100,38 @@ hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s
                          out_rows, a.n_split);
     return hipGetLastError();
   }
-  if (rows == 256) {
+  if (a.rows == 256) {
     if (scas)
-      hipLaunchKernelGGL((attend_q256_kernel<true, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attend_q256_kernel<true, false, PAGED, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
+    else if (pre)
+      hipLaunchKernelGGL((attend_q256_kernel<false, false, PAGED, true>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((attend_q256_kernel<false, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attend_q256_kernel<false, false, PAGED, false>), dim3(unsigned(blocks)), dim3(512), 0, s, a);
   } else {
     if (scas)
-      hipLaunchKernelGGL(attend_q128_kernel<true>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_q128_kernel<true, PAGED>), dim3(unsigned(blocks)), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(attend_q128_kernel<false>, dim3(unsigned(blocks)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attend_q128_kernel<false, PAGED>), dim3(unsigned(blocks)), dim3(256), 0, s, a);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attend_bf16_d128(const AttendArgs& a, bool scas, hipStream_t s) {
+  const int rows = a.rows;
+  const int64_t blocks = int64_t(a.B) * a.H * a.n_qtiles * a.n_split;
+  if ((rows != 128 && rows != 256) || a.n_qtiles != (a.n + rows - 1) / rows ||
+      (a.order && a.B % kXcds != 0))
+    return hipErrorInvalidValue;
+  if (a.n_split < 1 || a.n_split > kMaxSplits ||
+      (a.n_split > 1 && (scas || rows != 256 || !a.ws_o || !a.ws_ml)))
+    return hipErrorInvalidValue;
+  if ((a.map != nullptr) != (a.mapoff != nullptr) || (a.map && a.append))
+    return hipErrorInvalidValue;
+  if (!grid_fits(blocks, 512) || !grid_fits((int64_t(a.B) * a.n * a.H + 7) / 8, 256))
+    return hipErrorInvalidConfiguration;
+  return a.map ? launch_attend<true>(a, scas, s) : launch_attend<false>(a, scas, s);
 }
 
 }  // namespace hk

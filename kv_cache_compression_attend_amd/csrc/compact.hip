@@ -189,6 +189,57 @@ hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Pooled caches: the stored segments of a completed scale go to their pool
+// rows (one workgroup per (segment, batch entry, block of rows)); nothing
+// already in the pool moves.  Reads stride over the [B][n][H][D] source,
+// writes are whole 256-byte rows wherever the pool placed them.
+__global__ __launch_bounds__(kCopyThreads) void compact_pooled_kernel(PoolArgs a) {
+  const int chunk = blockIdx.x % a.chunks;
+  const int rest = blockIdx.x / a.chunks;
+  const int b = rest % a.B;
+  const PoolDesc d = a.desc[rest / a.B];
+  const int row0 = chunk * a.rows_per_block;
+  const int rows = min(a.rows_per_block, a.n - row0);
+  const int items = rows << a.cpr_shift;
+  const int cmask = (1 << a.cpr_shift) - 1;
+  const int64_t tok_stride = int64_t(a.H) * a.row_bytes;
+  const int64_t src0 = int64_t(d.layer - a.layer_begin) * a.layer_stride_bytes +
+                       (int64_t(b) * a.n + row0) * tok_stride + int64_t(d.head) * a.row_bytes;
+  const int64_t pool0 = int64_t(b) * a.pool_rows * a.row_bytes;
+  const int32_t* prow = a.rows + d.rows_first + row0;
+  u32x4 kv[kCopyItems], vv[kCopyItems];
+  int64_t dst[kCopyItems];
+#pragma unroll
+  for (int u = 0; u < kCopyItems; ++u) {
+    const int it = threadIdx.x + u * kCopyThreads;
+    if (it < items) {
+      const int r = it >> a.cpr_shift, c = it & cmask;
+      const int64_t off = src0 + r * tok_stride + c * 16;
+      kv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.kcur + off));
+      vv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.vcur + off));
+      dst[u] = pool0 + int64_t(prow[r]) * a.row_bytes + c * 16;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kCopyItems; ++u) {
+    const int it = threadIdx.x + u * kCopyThreads;
+    if (it < items) {
+      __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(a.kpool + dst[u]));
+      __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(a.vpool + dst[u]));
+    }
+  }
+}
+
+hipError_t launch_compact_pooled(const PoolArgs& a, hipStream_t s) {
+  const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
+  if (blocks == 0) return hipSuccess;
+  if ((16 << a.cpr_shift) != a.row_bytes || int64_t(a.rows_per_block) * a.row_bytes > kCopyBlockBytes)
+    return hipErrorInvalidValue;
+  if (!grid_fits(blocks, kCopyThreads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(compact_pooled_kernel, dim3(unsigned(blocks)), dim3(kCopyThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
   const int64_t blocks = int64_t(a.n_desc) * a.B * a.chunks;
   if (blocks == 0) return hipSuccess;

@@ -69,6 +69,17 @@ struct hk_ctx {
   hk::UnpackItem* d_uitems = nullptr;
   float2* d_qminmax = nullptr;        // split-quantizer workspace
   int64_t qminmax_slots = 0;          // its capacity in (desc, sub-block, chunk, b) slots
+  // Pooled cache: every head's rows in one pool of pool_rows rows per batch
+  // entry; d_map holds, per (step, layer, head), the pool row of each row the
+  // head holds while the step is attended (offsets d_mapoff [K][L][H]);
+  // pdesc_first[t*(L+1)+l] indexes the stored segments of (t, l) in d_pdesc.
+  bool pooled = false;
+  int64_t pool_rows = 0;
+  int32_t* d_map = nullptr;
+  int64_t* d_mapoff = nullptr;
+  int32_t* d_poolrows = nullptr;
+  hk::PoolDesc* d_pdesc = nullptr;
+  std::vector<int64_t> pdesc_first;
 };
 
 namespace {
@@ -116,6 +127,14 @@ void free_tables(hk_ctx* c) {
     c->kcache = nullptr;
     c->vcache = nullptr;
   }
+  (void)hipFree(c->d_map);
+  (void)hipFree(c->d_mapoff);
+  (void)hipFree(c->d_poolrows);
+  (void)hipFree(c->d_pdesc);
+  c->d_map = nullptr;
+  c->d_mapoff = nullptr;
+  c->d_poolrows = nullptr;
+  c->d_pdesc = nullptr;
   (void)hipFree(c->d_partials);
   (void)hipFree(c->d_ws_o);
   (void)hipFree(c->d_ws_ml);
@@ -157,6 +176,20 @@ int check_step_args(const hk_ctx* c, int layer, int step) {
 int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const void* k_cur,
                   const void* v_cur, int64_t layer_stride_elems, void* hip_stream);
 
+// A pooled cache gives the rows of segments dropped at step-1 and earlier
+// (by any layer), and at this step by the layers before this one, to the
+// segment appended here; their readers must be done: every layer has
+// appended step-1 (so it has attended it) and the layers before this one
+// have appended this step.
+int pool_append_order(const hk_ctx* c, int layer, int step) {
+  if (!c->pooled) return HK_OK;
+  for (int l = 0; l < c->L; ++l)
+    if (c->appended[l] < (l < layer ? step : step - 1))
+      return fail(HK_EORDER, "append(layer %d, step %d) on a pooled cache before layer %d has "
+                  "appended step %d", layer, step, l, l < layer ? step : step - 1);
+  return HK_OK;
+}
+
 int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_cur,
                   const void* v_cur, void* out, float softmax_scale, float* scas_table,
                   bool scas, bool append, void* hip_stream, double* scas_sum = nullptr) {
@@ -171,6 +204,11 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   if (step > 0 && c->appended[layer] < step - 1)
     return fail(HK_EORDER, "attend(layer %d, step %d) needs scale %d appended first (last: %d)",
                 layer, step, step - 1, c->appended[layer]);
+  // A pooled cache reuses the rows of dropped segments, so a step is attended
+  // only before its own append (its rows may be reused afterwards).
+  if (c->pooled && c->appended[layer] != step - 1)
+    return fail(HK_EORDER, "attend(layer %d, step %d) on a pooled cache after its append (last "
+                "appended: %d)", layer, step, c->appended[layer]);
   // Segments that leave the cache at a step are overwritten by that step's
   // append (the gather moves the survivors down): once the append of any
   // step u >= step that drops segments has run, this step's layout is gone.
@@ -184,6 +222,10 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   if (append && c->appended[layer] != step - 1)
     return fail(HK_EORDER, "append(layer %d, step %d) out of order (last appended: %d)", layer,
                 step, c->appended[layer]);
+  if (append) {
+    rc = pool_append_order(c, layer, step);
+    if (rc != HK_OK) return rc;
+  }
 
   DeviceGuard g(c->device);
   if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
@@ -202,6 +244,10 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   a.order = c->ordered[int64_t(step) * c->L + layer] ? c->d_order + (int64_t(step) * c->L + layer) * c->H
                                                       : nullptr;
   a.partials = c->d_partials;
+  if (c->pooled) {
+    a.map = c->d_map;
+    a.mapoff = c->d_mapoff + (int64_t(step) * c->L + layer) * c->H;
+  }
   a.ws_o = c->d_ws_o;
   a.ws_ml = c->d_ws_ml;
   a.rows = scas ? c->rows_scas[step] : c->rows[step];
@@ -218,7 +264,7 @@ int attend_common(hk_ctx* c, int layer, int step, const void* q, const void* k_c
   // step (segment t is then stored where the attention still reads, after
   // the survivors); otherwise the gather and compaction kernels run after the
   // attention kernel.
-  const bool fused = append && c->dtype == HK_DTYPE_BF16 && !drops && c->quant_m == 0;
+  const bool fused = append && c->dtype == HK_DTYPE_BF16 && !drops && c->quant_m == 0 && !c->pooled;
   a.append = fused;
 
   hipError_t e = hipSuccess;
@@ -266,7 +312,8 @@ namespace {
 // Builds a context for an expiry-step schedule.  quant_m > 0: 4-bit storage
 // in k_cache / v_cache (a static schedule, bf16 head_dim 128).
 int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* scale_tokens,
-                const uint8_t* expire, int dtype, void* k_cache, void* v_cache, int quant_m) {
+                const uint8_t* expire, int dtype, void* k_cache, void* v_cache, int quant_m,
+                bool pooled = false) {
   if (!out) return fail(HK_EINVAL, "null output pointer");
   *out = nullptr;
   if (L < 1 || H < 1 || B < 1 || K < 1) return fail(HK_EINVAL, "L, H, B, K must be >= 1");
@@ -287,8 +334,12 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
   if (bad >= 0)
     return fail(HK_EINVAL, "expire[%lld] = %d outside [scale, K-1]", (long long)bad, int(expire[bad]));
 
+  if (pooled && (dtype != HK_DTYPE_BF16 || D != 128 || quant_m > 0))
+    return fail(HK_EUNSUPPORTED, "pooled caches take bf16 tensors with head_dim 128");
+
   auto* c = new hk_ctx();
   c->L = L; c->H = H; c->D = D; c->B = B; c->K = K; c->dtype = dtype;
+  c->pooled = pooled;
   c->elem_bytes = dtype == HK_DTYPE_BF16 ? 2 : 4;
   c->tokens.assign(scale_tokens, scale_tokens + K);
   c->expire.assign(expire, expire + heads * K);
@@ -308,6 +359,22 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
     c->base[f] = offset;
     offset += c->cap[f] * B * D;
     scratch_elems = std::max(scratch_elems, offset);
+  }
+  hk::PoolPlan plan;
+  if (pooled) {
+    // One pool per batch entry shared by every head (base 0, cap = pool rows).
+    hk::pool_plan(expire, scale_tokens, L, H, K, plan);
+    if (plan.rows * D * c->elem_bytes > INT32_MAX) {
+      delete c;
+      return fail(HK_EINVAL, "pool of %lld rows exceeds 2^31 bytes per batch entry",
+                  (long long)plan.rows);
+    }
+    c->pool_rows = plan.rows;
+    for (int64_t f = 0; f < heads; ++f) {
+      c->base[f] = 0;
+      c->cap[f] = plan.rows;
+    }
+    offset = plan.rows * B * D;
   }
   const int64_t cache_bytes = quant_m > 0 ? 0 : offset * c->elem_bytes;
   std::vector<int64_t> code_base, param_base;
@@ -355,6 +422,14 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
       c->desc_first[int64_t(t) * (L + 1) + l] = int64_t(desc.size());
       c->gdesc_first[int64_t(t) * (L + 1) + l] = int64_t(gdesc.size());
       if (t > K - 2 || quant_m > 0) continue;
+      if (pooled) {
+        for (int h = 0; h < H; ++h) {
+          const int64_t f = int64_t(l) * H + h;
+          for (int sd = 0; sd < t; ++sd)
+            if (expire[f * K + sd] == t) c->drops[int64_t(t) * L + l] = 1;
+        }
+        continue;
+      }
       for (int h = 0; h < H; ++h) {
         const int64_t f = int64_t(l) * H + h;
         for (int sd = 0; sd < t; ++sd)
@@ -383,6 +458,38 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
     }
     c->desc_first[int64_t(t) * (L + 1) + L] = int64_t(desc.size());
     c->gdesc_first[int64_t(t) * (L + 1) + L] = int64_t(gdesc.size());
+  }
+
+  // Pooled cache: the map of every (step, layer, head) -- the pool rows of
+  // the segments the head holds while the step is attended, in scale order
+  // -- and one descriptor per stored segment.
+  std::vector<int32_t> map;
+  std::vector<int64_t> mapoff;
+  std::vector<hk::PoolDesc> pdesc;
+  c->pdesc_first.assign(int64_t(K) * (L + 1), 0);
+  if (pooled) {
+    mapoff.assign(int64_t(K) * heads, 0);
+    for (int t = 0; t < K; ++t) {
+      for (int64_t f = 0; f < heads; ++f) {
+        mapoff[int64_t(t) * heads + f] = int64_t(map.size());
+        for (int sd = 0; sd < t && sd <= K - 2; ++sd) {
+          const int64_t first = plan.seg_first[f * K + sd];
+          if (first < 0 || expire[f * K + sd] < t) continue;
+          map.insert(map.end(), plan.rows_of.begin() + first,
+                     plan.rows_of.begin() + first + scale_tokens[sd]);
+        }
+      }
+      for (int l = 0; l < L; ++l) {
+        c->pdesc_first[int64_t(t) * (L + 1) + l] = int64_t(pdesc.size());
+        if (t > K - 2) continue;
+        for (int h = 0; h < H; ++h) {
+          const int64_t f = int64_t(l) * H + h;
+          if (plan.seg_first[f * K + t] >= 0)
+            pdesc.push_back(hk::PoolDesc{plan.seg_first[f * K + t], h, l});
+        }
+      }
+      c->pdesc_first[int64_t(t) * (L + 1) + L] = int64_t(pdesc.size());
+    }
   }
 
   // 4-bit storage: one quantize descriptor per stored (t, l, h); unpack
@@ -504,6 +611,10 @@ int create_impl(hk_ctx** out, int L, int H, int D, int B, int K, const int32_t* 
   if (e == hipSuccess) e = upload(&c->d_gruns, gruns);
   if (e == hipSuccess) e = upload(&c->d_qdesc, qdesc);
   if (e == hipSuccess) e = upload(&c->d_uitems, uitems);
+  if (e == hipSuccess && pooled) e = upload(&c->d_map, map);
+  if (e == hipSuccess && pooled) e = upload(&c->d_mapoff, mapoff);
+  if (e == hipSuccess && pooled) e = upload(&c->d_poolrows, plan.rows_of);
+  if (e == hipSuccess && pooled) e = upload(&c->d_pdesc, pdesc);
   if (e == hipSuccess && c->qminmax_slots > 0)
     e = hipMalloc(reinterpret_cast<void**>(&c->d_qminmax),
                   size_t(c->qminmax_slots) * 2 * hk::kQuantD * sizeof(float2));
@@ -534,6 +645,13 @@ extern "C" int hk_create_expiry(hk_ctx** out, int L, int H, int D, int B, int K,
                                 const int32_t* scale_tokens, const uint8_t* expire, int dtype,
                                 void* k_cache, void* v_cache) {
   return create_impl(out, L, H, D, B, K, scale_tokens, expire, dtype, k_cache, v_cache, 0);
+}
+
+extern "C" int hk_create_pooled(hk_ctx** out, int L, int H, int D, int B, int K,
+                                const int32_t* scale_tokens, const uint8_t* expire, void* k_pool,
+                                void* v_pool) {
+  return create_impl(out, L, H, D, B, K, scale_tokens, expire, HK_DTYPE_BF16, k_pool, v_pool, 0,
+                     true);
 }
 
 extern "C" int hk_create_int4(hk_ctx** out, int L, int H, int D, int B, int K,
@@ -634,6 +752,8 @@ extern "C" int hk_append_scale(hk_ctx* c, int layer_begin, int layer_end, int st
       return fail(HK_EORDER, "append(layer %d, step %d) overwrites segments that attend(layer %d, "
                   "step %d) reads: attend first", l, step, l, step);
   }
+  const int rc = pool_append_order(c, layer_begin, step);
+  if (rc != HK_OK) return rc;
   return append_launch(c, layer_begin, layer_end, step, k_cur, v_cur, layer_stride_elems,
                        hip_stream);
 }
@@ -671,6 +791,37 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
       q.minmax = c->d_qminmax;
       hipError_t e = hk::launch_quantize(q, static_cast<hipStream_t>(hip_stream));
       if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    }
+    for (int l = layer_begin; l < layer_end; ++l) c->appended[l] = step;
+    return HK_OK;
+  }
+  if (c->pooled) {
+    const int64_t pf = c->pdesc_first[int64_t(step) * (c->L + 1) + layer_begin];
+    const int64_t pl = c->pdesc_first[int64_t(step) * (c->L + 1) + layer_end];
+    if (pl > pf) {
+      DeviceGuard g(c->device);
+      if (!g.ok) return fail(HK_EHIP, "cannot select device %d", c->device);
+      hk::PoolArgs a{};
+      a.desc = c->d_pdesc + pf;
+      a.rows = c->d_poolrows;
+      a.kcur = static_cast<const uint8_t*>(k_cur);
+      a.vcur = static_cast<const uint8_t*>(v_cur);
+      a.kpool = static_cast<uint8_t*>(c->kcache);
+      a.vpool = static_cast<uint8_t*>(c->vcache);
+      a.layer_stride_bytes = nl > 1 ? layer_stride_elems * c->elem_bytes : 0;
+      a.pool_rows = c->pool_rows;
+      a.n_desc = int(pl - pf);
+      a.B = c->B;
+      a.n = c->tokens[step];
+      a.H = c->H;
+      a.layer_begin = layer_begin;
+      a.row_bytes = c->D * c->elem_bytes;
+      a.cpr_shift = 0;
+      while ((16 << a.cpr_shift) < a.row_bytes) ++a.cpr_shift;
+      a.rows_per_block = std::min(hk::kCopyBlockBytes / a.row_bytes, a.n);
+      a.chunks = (a.n + a.rows_per_block - 1) / a.rows_per_block;
+      hipError_t e = hk::launch_compact_pooled(a, static_cast<hipStream_t>(hip_stream));
+      if (e != hipSuccess) return hip_fail(e, "compact launch");
     }
     for (int l = layer_begin; l < layer_end; ++l) c->appended[l] = step;
     return HK_OK;

@@ -65,6 +65,32 @@ struct RowsArgs {
   int rows;               // tokens per workgroup
 };
 
+// One stored (layer, head) segment of a completed scale in a pooled cache:
+// its n rows go to pool rows rows[rows_first + i], i < n (the same rows in
+// every batch entry's pool).
+struct PoolDesc {
+  int64_t rows_first;
+  int32_t head;
+  int32_t layer;
+};
+
+struct PoolArgs {
+  const PoolDesc* desc;   // descriptors of this launch
+  const int32_t* rows;    // pool rows of every stored segment
+  const uint8_t* kcur;    // byte views, [B][n][H][D] per layer
+  const uint8_t* vcur;
+  uint8_t* kpool;         // [B][pool_rows][D]
+  uint8_t* vpool;
+  int64_t layer_stride_bytes;
+  int64_t pool_rows;
+  int n_desc, B, n, H;
+  int layer_begin;        // layer whose tensor starts at kcur / vcur
+  int row_bytes;          // 16 << cpr_shift
+  int cpr_shift;
+  int rows_per_block;     // kCopyBlockBytes / row_bytes
+  int chunks;             // row blocks per (desc, b)
+};
+
 // One (layer, head) whose cache loses segments at a step: the held segments
 // that outlive the step move down over the dropped ones.  The moves are runs
 // (dst row, src row, rows) in ascending order with dst < src, covering
@@ -157,6 +183,7 @@ hipError_t launch_scas_accumulate(const float* partials, double* table, int laye
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_compact_rows(const RowsArgs& a, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t launch_compact_pooled(const PoolArgs& a, hipStream_t s);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t s);
 hipError_t launch_unpack(const UnpackArgs& a, hipStream_t s);
 

@@ -124,4 +124,79 @@ inline int64_t int4_layout(const uint8_t* keep, const std::vector<int64_t>& cap,
   return off;
 }
 
+// One pool of rows shared by every head (per batch entry and per K or V
+// buffer), for schedules whose segments leave the cache after they were
+// stored: rows freed by a dropped segment are reused by later segments, so
+// nothing ever moves and the pool holds exactly the most token slots the
+// cache holds at once.  Events are taken in generation order -- for each
+// scale k, for each layer l: the queries of (l, k) read the cache, then the
+// segments of layer l that expire at k give back their rows and the stored
+// segments (l, h, k) take rows -- the order of the per-layer accounting of
+// Algorithm 2 (Pith page of arXiv 2605.14877, Appendix A).  Rows are taken
+// lowest first, so a segment is one run of consecutive rows unless it fills
+// holes.
+struct PoolPlan {
+  int64_t rows = 0;                // pool rows per batch entry
+  std::vector<int64_t> seg_first;  // [heads][K]: first entry in rows_of, -1 if not stored
+  std::vector<int32_t> rows_of;    // pool rows of the stored segments, in event order
+};
+
+inline void pool_plan(const uint8_t* expire, const int32_t* tokens, int L, int H, int K,
+                      PoolPlan& p) {
+  const int64_t heads = int64_t(L) * H;
+  p.rows = 0;
+  p.seg_first.assign(heads * K, -1);
+  p.rows_of.clear();
+  std::vector<std::pair<int64_t, int64_t>> free_runs;  // (start, length), sorted by start
+  auto give_back = [&](int64_t first, int n) {
+    // the segment's rows as runs of consecutive rows
+    int i = 0;
+    while (i < n) {
+      int j = i + 1;
+      while (j < n && p.rows_of[first + j] == p.rows_of[first + j - 1] + 1) ++j;
+      const int64_t a = p.rows_of[first + i], len = j - i;
+      auto it = std::lower_bound(free_runs.begin(), free_runs.end(), std::make_pair(a, int64_t(0)));
+      it = free_runs.insert(it, {a, len});
+      // merge with the next and the previous run
+      if (it + 1 != free_runs.end() && it->first + it->second == (it + 1)->first) {
+        it->second += (it + 1)->second;
+        free_runs.erase(it + 1);
+      }
+      if (it != free_runs.begin() && (it - 1)->first + (it - 1)->second == it->first) {
+        (it - 1)->second += it->second;
+        free_runs.erase(it);
+      }
+      i = j;
+    }
+  };
+  auto take = [&](int n) {
+    const int64_t first = int64_t(p.rows_of.size());
+    while (n > 0 && !free_runs.empty()) {
+      auto& r = free_runs.front();
+      const int64_t m = std::min<int64_t>(n, r.second);
+      for (int64_t q = 0; q < m; ++q) p.rows_of.push_back(int32_t(r.first + q));
+      r.first += m;
+      r.second -= m;
+      n -= int(m);
+      if (r.second == 0) free_runs.erase(free_runs.begin());
+    }
+    for (; n > 0; --n) p.rows_of.push_back(int32_t(p.rows++));
+    return first;
+  };
+  for (int k = 0; k < K; ++k)
+    for (int l = 0; l < L; ++l) {
+      for (int h = 0; h < H; ++h) {
+        const int64_t f = int64_t(l) * H + h;
+        for (int s = 0; s < k && s <= K - 2; ++s)
+          if (expire[f * K + s] == k && p.seg_first[f * K + s] >= 0)
+            give_back(p.seg_first[f * K + s], tokens[s]);
+      }
+      if (k > K - 2) continue;
+      for (int h = 0; h < H; ++h) {
+        const int64_t f = int64_t(l) * H + h;
+        if (expire[f * K + k] > k) p.seg_first[f * K + k] = take(tokens[k]);
+      }
+    }
+}
+
 }  // namespace hk

@@ -207,6 +207,37 @@ extern "C" int hk_layout_expiry(int L, int H, int K, const int32_t* scale_tokens
   return HK_OK;
 }
 
+extern "C" int hk_layout_pooled(int L, int H, int K, const int32_t* scale_tokens,
+                                const uint8_t* expire, int B, int D, int64_t* pool_elems_out,
+                                int64_t* pool_rows_out, int32_t* seg_rows_out) {
+  if (L < 1 || H < 1 || K < 1 || B < 1 || D < 1) return fail(HK_EINVAL, "sizes must be >= 1");
+  if (!scale_tokens || !expire || !pool_elems_out) return fail(HK_EINVAL, "null argument");
+  for (int s = 0; s < K; ++s)
+    if (scale_tokens[s] < 1) return fail(HK_EINVAL, "scale %d has no tokens", s);
+  const int64_t heads = int64_t(L) * H;
+  const int64_t bad = hk::first_bad_expire(expire, heads, K);
+  if (bad >= 0)
+    return fail(HK_EINVAL, "expire[%lld] = %d outside [scale, K-1]", (long long)bad, int(expire[bad]));
+  hk::PoolPlan p;
+  hk::pool_plan(expire, scale_tokens, L, H, K, p);
+  if (p.rows > INT32_MAX) return fail(HK_EINVAL, "pool exceeds 2^31 rows");
+  *pool_elems_out = p.rows * B * D;
+  if (pool_rows_out) *pool_rows_out = p.rows;
+  if (seg_rows_out) {
+    int64_t per_head = 0;
+    for (int s = 0; s <= K - 2; ++s) per_head += scale_tokens[s];
+    for (int64_t f = 0; f < heads; ++f) {
+      int64_t off = f * per_head;
+      for (int s = 0; s <= K - 2; ++s) {
+        const int64_t first = p.seg_first[f * K + s];
+        for (int i = 0; i < scale_tokens[s]; ++i) seg_rows_out[off + i] = first >= 0 ? p.rows_of[first + i] : -1;
+        off += scale_tokens[s];
+      }
+    }
+  }
+  return HK_OK;
+}
+
 extern "C" int hk_layout_int4(int L, int H, int K, const int32_t* scale_tokens,
                               const uint8_t* keep, int B, int D, int sub_blocks,
                               int64_t* store_bytes_out, int64_t* param_offset_out) {

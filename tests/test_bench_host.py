@@ -92,7 +92,7 @@ def test_trace_summary_takes_the_final_scale_launches(bench, tmp_path):
     hdr = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp",
            "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
     k = "void hk::(anonymous namespace)::" + bench.ROOFLINE_KERNEL + "(hk::AttendArgs)"
-    split = "void hk::(anonymous namespace)::attend_q256_kernel<false, true>(hk::AttendArgs)"
+    split = "void hk::(anonymous namespace)::attend_q256_kernel<false, true, false, true>(hk::AttendArgs)"
     rows = [["KERNEL_DISPATCH", 1, k, 0, 9000, 8192, 1, 1],         # a small scale
             ["KERNEL_DISPATCH", 2, split, 0, 500000, 221184, 1, 1],  # a split launch, larger grid
             ["KERNEL_DISPATCH", 3, k, 100, 330100, 131072, 1, 1],
@@ -138,7 +138,7 @@ def test_pass_summary_takes_the_fused_passes(bench, tmp_path):
     hdr = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp",
            "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
     k = "void hk::(anonymous namespace)::" + bench.ROOFLINE_KERNEL + "(hk::AttendArgs)"
-    small = "void hk::(anonymous namespace)::attend_q128_kernel<false>(hk::AttendArgs)"
+    small = "void hk::(anonymous namespace)::attend_q128_kernel<false, false>(hk::AttendArgs)"
     rows, t, did = [], 0, 0
 
     def add(name, dur, grid):
@@ -158,6 +158,6 @@ def test_pass_summary_takes_the_fused_passes(bench, tmp_path):
     _write_csv(path, hdr, rows)
     s = bench.summarize_pass(str(path))
     assert s["passes"] == 3
-    assert [x["kernel"] for x in s["launches"]] == ["attend_q128_kernel<false>", bench.ROOFLINE_KERNEL]
+    assert [x["kernel"] for x in s["launches"]] == ["attend_q128_kernel<false, false>", bench.ROOFLINE_KERNEL]
     assert [x["median_us"] for x in s["launches"]] == [6.0, 330.0]
     assert s["sum_median_us"] == 336.0

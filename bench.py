@@ -37,7 +37,7 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 ATTEND_SOURCES = ["kv_cache_compression_attend_amd/csrc/attend_bf16.hip",
                   "kv_cache_compression_attend_amd/csrc/attend.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attend_q256_infinity2b_layer_traffic.json")
-ROOFLINE_KERNEL = "attend_q256_kernel<false, false>"
+ROOFLINE_KERNEL = "attend_q256_kernel<false, false, false, true>"
 
 
 def attend_sources_sha() -> str:
@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--no-pruned", action="store_true",
                     help="skip the 32-layer 10%%-budget scales/s measurement")
     ap.add_argument("--pruned-steps", type=int, default=5)
+    ap.add_argument("--sections", default="all",
+                    help="comma-separated workload sections after the main line (pruned, "
+                         "progressive, window, int4, compact, infinity8b_4pct, "
+                         "infinity8b_full_cache, calibration) or 'all'")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run three 1 GiB device-to-device copies (calibrates HBM byte counters)")
     ap.add_argument("--summarize-pass", metavar="KERNEL_TRACE_CSV",
@@ -73,10 +77,18 @@ def parse():
                     help="time the final-scale attend launch of the main workload on its random "
                          "inputs, with V zeroed, and with K and V zeroed (same instructions, less "
                          "operand toggling), then exit")
-    ap.add_argument("--cpu-passes", type=int, default=3,
-                    help="passes of the oracle over the sample (the whole layer takes ~4 s)")
+    ap.add_argument("--cpu-passes", type=int, default=1,
+                    help="passes of the oracle over the main workload (the whole layer takes ~4 s)")
     ap.add_argument("--cpu-heads", type=int, default=16,
                     help="heads of the full-cache layer the CPU oracle runs (all 13 scales)")
+    ap.add_argument("--sections-only", action="store_true",
+                    help="run only the sections named by --sections (no main line, no CPU "
+                         "baseline) and print their JSON")
+    ap.add_argument("--summarize-compact-counters", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print the HBM traffic of the compaction kernels per pass of the compact "
+                         "section (--sections-only --sections compact) from rocprofv3 counter CSVs, "
+                         "then exit")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
                                                               "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="print the HBM traffic profile of the final-scale attend launch from "
@@ -200,6 +212,65 @@ def summarize_counters(paths):
                 "<w>/run_counter_collection.csv <cf>/run_counter_collection.csv <cw>/run_counter_collection.csv"]}
 
 
+def summarize_compact_counters(paths):
+    """HBM traffic of the compaction kernels over the compact section's
+    passes (all-layer appends of the 32-layer batch-4 full-cache workload,
+    13.47 GB algorithmic per pass), scaled by the copy-probe counters."""
+    import csv
+
+    def totals(path, match):
+        vals, grid = {}, {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if match(r["Kernel_Name"]):
+                    key = r["Dispatch_Id"]
+                    vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+                    grid[key] = (r["Kernel_Name"], int(r["Grid_Size"]))
+        return vals, grid
+
+    def is_compact(name):
+        return "compact_rows_kernel" in name or "compact_kernel" in name
+
+    def copy_kib(path):
+        vals, _ = totals(path, lambda n: "copyBuffer" in n)
+        if not vals:
+            raise SystemExit(f"no copy dispatch in {path}")
+        return sum(vals.values()) / len(vals)
+
+    fv, fg = totals(paths[0], is_compact)
+    wv, wg = totals(paths[1], is_compact)
+    if not fv or not wv:
+        raise SystemExit("no compaction dispatch")
+    # passes: dispatches of the largest grid (one per pass, the largest scale)
+    top = max(g for _, g in fg.values())
+    passes = sum(1 for _, g in fg.values() if g == top)
+    fs, ws = float(1 << 20) / copy_kib(paths[2]), float(1 << 20) / copy_kib(paths[3])
+    fetch = sum(fv.values()) * fs * 1024 / passes
+    write = sum(wv.values()) * ws * 1024 / passes
+    per_kernel = {}
+    for d, (n, _) in fg.items():
+        short = "compact_rows_kernel" if "compact_rows_kernel" in n else "compact_kernel"
+        per_kernel.setdefault(short, [0, 0.0, 0.0])
+        per_kernel[short][0] += 1
+        per_kernel[short][1] += fv[d] * fs * 1024 / passes
+        per_kernel[short][2] += wv.get(d, 0.0) * ws * 1024 / passes
+    algo = 13.47e9
+    return {"workload": "infinity2b-l32-b4 full cache: one all-layer append per completed scale",
+            "passes": passes, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "read_bytes_per_pass": int(fetch), "write_bytes_per_pass": int(write),
+            "bytes_per_pass": int(fetch + write), "algorithmic_bytes_per_pass": algo,
+            "ratio_to_algorithmic": round((fetch + write) / algo, 4),
+            "per_kernel": {k: {"dispatches_per_pass": v[0] / passes, "read_bytes": int(v[1]),
+                               "write_bytes": int(v[2])} for k, v in per_kernel.items()},
+            "commands": [
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o run -- python3 <repo>/bench.py --sections-only --sections compact",
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o run -- python3 <repo>/bench.py --sections-only --sections compact",
+                "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <cf> -o run -- python3 <repo>/bench.py --copy-probe",
+                "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <cw> -o run -- python3 <repo>/bench.py --copy-probe",
+                "python3 <repo>/bench.py --summarize-compact-counters <f>/run_counter_collection.csv "
+                "<w>/run_counter_collection.csv <cf>/run_counter_collection.csv <cw>/run_counter_collection.csv"]}
+
+
 def pass_flops(wl, keep, lenb_fn):
     """Algorithmic attention flops of each (layer, step) launch: sum over (b, h)
     of 4 * d * n_t * (cached keys + n_t)."""
@@ -274,6 +345,9 @@ def main():
     if args.summarize_counters:
         print(json.dumps(summarize_counters(args.summarize_counters), indent=1))
         return
+    if args.summarize_compact_counters:
+        print(json.dumps(summarize_compact_counters(args.summarize_compact_counters), indent=1))
+        return
     if args.summarize_pass:
         print(json.dumps(summarize_pass(args.summarize_pass), indent=1))
         return
@@ -303,6 +377,44 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_each": src.numel() * 2, "copies": 3}), flush=True)
+        return
+
+    # ---------------- the other workloads ----------------
+    # They run first: the GPU then reaches its sustained clock (it needs ~100
+    # ms of work after the host-side set-up) before the main line's timed
+    # passes, whatever the number of warmup passes.
+    result = {}
+    sections = {"pruned", "progressive", "window", "int4", "compact", "infinity8b_4pct",
+                "infinity8b_full_cache", "calibration"}
+    want = sections if args.sections == "all" else set(args.sections.split(","))
+    unknown = want - sections
+    if unknown:
+        raise SystemExit(f"unknown sections {sorted(unknown)}")
+    if args.no_pruned or args.data_sensitivity:
+        want = set()
+    # 32 layers, batch 8, 10% budget: scales/s per image
+    if "pruned" in want:
+        result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
+    if "progressive" in want:
+        result["progressive_10pct"] = progressive_rate(args, hk, workloads, torch, np, dev, stream)
+    if "window" in want:
+        result["scale_window"] = window_rate(args, hk, workloads, torch, np, dev, stream)
+    if "int4" in want:
+        result["int4_10pct"] = int4_rate(args, hk, workloads, torch, np, dev, stream)
+    if "compact" in want:
+        result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
+    if "infinity8b_4pct" in want:
+        result["infinity8b_4pct"] = infinity8b_rate(args, hk, workloads, torch, np, dev, stream,
+                                                    full_cache=False)
+    if "infinity8b_full_cache" in want:
+        result["infinity8b_full_cache"] = infinity8b_rate(args, hk, workloads, torch, np, dev,
+                                                          stream, full_cache=True)
+    # calibration: S-CAS cost and ranking stability
+    if "calibration" in want:
+        result["calibration"] = calibration_rate(args, hk, workloads, torch, np, dev, stream)
+
+    if args.sections_only:
+        print(json.dumps(result), flush=True)
         return
 
     # ---------------- main workload: one full-cache Infinity-2B-shaped layer ----------------
@@ -373,6 +485,10 @@ def main():
         for t in range(K):
             for l in range(L):
                 rec[("a", l, t)] = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        # A sleep kernel ahead of the pass lets the host queue every launch
+        # and event before the GPU reaches them, so the events time the
+        # launches and not the host's calls between them.
+        gpu_sleep(torch)
         one_pass(rec)
         recs.append(rec)
     torch.cuda.synchronize()
@@ -408,6 +524,7 @@ def main():
             traffic = tr.get("bytes_per_launch")
 
     value = total_flops / (ms_pass * 1e-3) / 1e12
+    sections_out = result
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -445,27 +562,43 @@ def main():
     ctx.close()
     del qs, kall, vall, outs
     torch.cuda.empty_cache()
-
-    # ---------------- 32 layers, batch 8, 10% budget: scales/s per image ----------------
-    if not args.no_pruned:
-        result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
-        result["progressive_10pct"] = progressive_rate(args, hk, workloads, torch, np, dev, stream)
-        result["scale_window"] = window_rate(args, hk, workloads, torch, np, dev, stream)
-        result["int4_10pct"] = int4_rate(args, hk, workloads, torch, np, dev, stream)
-        result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
-        result["infinity8b_4pct"] = infinity8b_rate(args, hk, workloads, torch, np, dev, stream,
-                                                    full_cache=False)
-        result["infinity8b_full_cache"] = infinity8b_rate(args, hk, workloads, torch, np, dev,
-                                                          stream, full_cache=True)
-
-    # ---------------- calibration: S-CAS cost and ranking stability ----------------
-    if not args.no_pruned:
-        result["calibration"] = calibration_rate(args, hk, workloads, torch, np, dev, stream)
+    result.update(sections_out)
 
     # ---------------- fp64 CPU oracle on a bounded sample ----------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, keep)
     print(json.dumps(result), flush=True)
+
+
+def gpu_sleep(torch, ms=3.0):
+    """Keeps the GPU busy for about `ms` (a spin kernel) so that the host can
+    queue a whole pass of launches and events behind it."""
+    torch.cuda._sleep(int(ms * 2.4e6))
+
+
+def step_profile(ctx, K, L, call, flops, stream, torch, passes=2):
+    """Per-step time of a whole pass (HIP events at the step boundaries on the
+    launch stream, mean over passes) and the step's attention TFLOP/s (its
+    launches over all layers, compaction fused where the call fuses it)."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    ms = [0.0] * K
+    for _ in range(passes):
+        ctx.reset()
+        gpu_sleep(torch)
+        for t in range(K):
+            ev[t].record(stream)
+            for l in range(L):
+                call(l, t)
+        ev[K].record(stream)
+        torch.cuda.synchronize()
+        for t in range(K):
+            ms[t] += ev[t].elapsed_time(ev[t + 1]) / passes
+    out = {}
+    for t in range(K):
+        f = sum(flops[(l, t)] for l in range(L))
+        out[t] = {"ms": round(ms[t], 4), "tflops": round(f / (ms[t] * 1e-3) / 1e12, 1),
+                  "plan": list(ctx.attend_plan(t))}
+    return out
 
 
 def pruned_rate(args, hk, workloads, torch, np, dev, stream):
@@ -504,6 +637,9 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.pruned_steps
+    steps = step_profile(ctx, K, L, lambda l, t: ctx.attend_append(
+        l, t, qs[t][l], kall[t][l], vall[t][l], outs[t], wl.softmax_scale, stream=stream),
+        flops, stream, torch)
     ctx.close()
     return {"workload": "infinity2b-l32-b8-budget10: 32 layers x 16 heads x d128, batch 8, "
                         f"10% budget ({n_pruned} of 512 heads pruned per prunable scale)",
@@ -512,6 +648,7 @@ def pruned_rate(args, hk, workloads, torch, np, dev, stream):
             "image_scales_per_sec": round(K * wl.batch / (ms * 1e-3), 1),
             "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
             "passes": args.pruned_steps,
+            "per_step": steps,
             "inputs": "torch.randn on the GPU (seeded), same distribution as the parity inputs"}
 
 
@@ -560,6 +697,9 @@ def infinity8b_rate(args, hk, workloads, torch, np, dev, stream, full_cache):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / passes
+    steps = step_profile(ctx, K, L, lambda l, t: ctx.attend_append(
+        l, t, qs[t], ks[t], vs[t], outs[t], wl.softmax_scale, stream=stream),
+        flops, stream, torch, passes=1)
     cache_gb = 2.0 * ctx.cache_elems * 2 / 1e9
     ctx.close()
     del qs, ks, vs, outs
@@ -575,6 +715,7 @@ def infinity8b_rate(args, hk, workloads, torch, np, dev, stream, full_cache):
             "compaction_gb_per_pass": round(copied / 1e9, 2),
             "cache_GB": round(cache_gb, 2),
             "passes": passes,
+            "per_step": steps,
             "inputs": "one seeded torch.randn draw of Q, K, V per scale, shared by the 40 layers"}
 
 
@@ -626,6 +767,7 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
     flops = pass_flops(wl, None, held_table(expire, wl.scale_tokens))
     static_flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
     ms, cache_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3)
+    ms_pool, pool_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3, pooled=True)
     row_bytes = wl.head_dim * 2
     gather_bytes = sum(moved_rows(expire, wl.scale_tokens, t) for t in range(K)) * wl.batch \
         * row_bytes * 2 * 2
@@ -634,27 +776,36 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
     return {"workload": "infinity2b-l32-b8-budget10-progressive: 32 layers x 16 heads x d128, "
                         "batch 8, 10% budget, lazy prefix lengths with per-layer accounting",
             "prefix_per_step": [int(x) for x in prefix],
-            "ms_per_pass": round(ms, 3),
-            "scales_per_sec_per_image": round(K / (ms * 1e-3), 1),
-            "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms * 1e-3) / 1e12, 1),
+            "ms_per_pass": round(ms_pool, 3),
+            "scales_per_sec_per_image": round(K / (ms_pool * 1e-3), 1),
+            "attend_tflops_incl_compaction": round(sum(flops.values()) / (ms_pool * 1e-3) / 1e12, 1),
             "attend_flops_vs_static": round(sum(flops.values()) / sum(static_flops.values()), 3),
-            "gather_bytes_per_pass": float(gather_bytes),
+            "gather_bytes_per_pass_per_head_regions": float(gather_bytes),
             "live_peak_token_slots": int(live.max()),
             "budget_token_slots": budget_slots,
             "live_peak_GB": round(int(live.max()) * slot_bytes / 1e9, 3),
-            "allocated_cache_GB": round(cache_bytes / 1e9, 3),
+            "budget_GB": round(budget_slots * slot_bytes / 1e9, 3),
+            "allocated_cache_GB": round(pool_bytes / 1e9, 3),
+            "allocation": "one pool shared by every head (rows of dropped segments reused, "
+                          "nothing moved)",
+            "per_head_regions": {"allocated_cache_GB": round(cache_bytes / 1e9, 3),
+                                 "ms_per_pass": round(ms, 3),
+                                 "note": "each head sized to its own peak; dropped segments "
+                                         "removed by an in-place gather"},
             "static_allocated_cache_GB": round(hk.layout(wl.scale_tokens, keep, wl.batch,
                                                          wl.head_dim)[0] * 2 * 2 / 1e9, 3),
             "passes": args.pruned_steps}
 
 
-def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed, keep=None, sub_blocks=None):
+def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed, keep=None, sub_blocks=None,
+                pooled=False):
     """Mean time of whole passes (every layer and scale, attend_append) under
-    an expiry schedule (or a keep-mask with 4-bit storage), on seeded GPU
-    inputs of the workload's shapes.  Returns (ms, bytes of the K and V caches)."""
+    an expiry schedule (per-head regions, or one pool shared by every head),
+    or a keep-mask with 4-bit storage, on seeded GPU inputs of the workload's
+    shapes.  Returns (ms, bytes of the K and V caches)."""
     if sub_blocks is None:
         ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, None,
-                         torch.bfloat16, expire=expire)
+                         torch.bfloat16, expire=expire, pooled=pooled)
         cache_bytes = ctx.cache_elems * 2 * 2
     else:
         ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
@@ -849,34 +1000,84 @@ def compact_rate(args, hk, workloads, torch, np, dev, stream):
             "per_step_GBps": {t: round(nbytes[t] / (ms[t] * 1e-3) / 1e9, 1) for t in ms}}
 
 
-def cpu_baseline(args, wl, keep):
-    """The fp64 oracle, as it stands, on every scale of the first few heads."""
-    import numpy as np
-    from threadpoolctl import threadpool_info
-
+def _oracle_sample(wl, keep, layer, batches, heads, passes=1, with_scas=False):
+    """Runs the fp64 oracle over every scale of the given (batch entry, head)
+    units of one layer; returns (algorithmic flops, seconds)."""
     import workloads
     from oracle import attention as oatt
     from oracle.numerics import to_f64
 
-    heads = list(range(min(args.cpu_heads, wl.heads)))
-    passes = max(1, args.cpu_passes)
-    steps = [workloads.step_inputs(wl, 0, t) for t in range(wl.n_scales)]
+    steps = [workloads.step_inputs(wl, layer, t, batch=max(batches) + 1) for t in range(wl.n_scales)]
     flops = 0.0
     start = time.perf_counter()
     for _ in range(passes):
         for t in range(wl.n_scales):
-            for h in heads:
-                kj, vj, src, lens = oatt.gather_keys([s.k for s in steps[: t + 1]],
-                                                     [s.v for s in steps[: t + 1]], keep[0, h], t, 0, h)
-                q = to_f64(steps[t].q[0, :, h, :], "bf16")
-                oatt.softmax_attention(q, to_f64(kj, "bf16"), to_f64(vj, "bf16"), wl.softmax_scale)
-                flops += 4.0 * wl.head_dim * q.shape[0] * kj.shape[0]
-    secs = time.perf_counter() - start
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": round(secs, 2),
-            "sample": f"full-cache layer, batch 1, all 13 scales of heads {heads[0]}..{heads[-1]} "
-                      f"({len(heads)} of {wl.heads}), fp64 NumPy, {passes} passes"}
+            for b in batches:
+                for h in heads:
+                    kj, vj, src, lens = oatt.gather_keys([s.k for s in steps[: t + 1]],
+                                                         [s.v for s in steps[: t + 1]], keep[layer, h],
+                                                         t, b, h)
+                    q = to_f64(steps[t].q[b, :, h, :], wl.dtype)
+                    _, prob = oatt.softmax_attention(q, to_f64(kj, wl.dtype), to_f64(vj, wl.dtype),
+                                                     wl.softmax_scale)
+                    if with_scas:
+                        oatt.segment_mass(prob, src, lens, t)
+                    flops += 4.0 * wl.head_dim * q.shape[0] * kj.shape[0]
+    return flops, time.perf_counter() - start
+
+
+def _oracle_keep(wl):
+    """The workload's keep-mask, built by the oracle's own schedule."""
+    import workloads
+    from oracle import schedule as osch
+    if wl.schedule == "random_drop2":
+        return workloads.random_drop2_keep(wl)
+    if wl.schedule == "full":
+        return workloads.full_keep(wl)
+    return osch.build_schedule(workloads.dirichlet_scas(wl), wl.scale_tokens, wl.budget, wl.n_sink)[0]
+
+
+def cpu_baseline(args, wl, keep):
+    """The fp64 oracle, as it stands, on the host cores: the main workload's
+    whole pass, and a bounded sample of every other workload, whose time for
+    the whole workload is extrapolated by algorithmic flops (labelled)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads
+
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    host = len(os.sched_getaffinity(0))
+    heads = list(range(min(args.cpu_heads, wl.heads)))
+    passes = max(1, args.cpu_passes)
+    flops, secs = _oracle_sample(wl, keep, 0, [0], heads, passes=passes)
+    out = {"value": round(flops / secs / 1e12, 5), "unit": "TFLOP/s", "cores": host,
+           "blas_threads": int(blas), "kind": "oracle", "seconds": round(secs, 2),
+           "sample": f"full-cache layer, batch 1, all 13 scales of heads {heads[0]}..{heads[-1]} "
+                     f"({len(heads)} of {wl.heads}), fp64 NumPy, {passes} pass(es)"}
+    per = {}
+    # (workload, layer, batch entries, heads, S-CAS) of each sample
+    plan = [("c0", 0, [0], None, True), ("c2", 0, [0], 8, False), ("c3", 0, [0], None, True),
+            ("c4", 0, [0], 8, False)]
+    for key, layer, batches, nh, scas in plan:
+        w = workloads.get(key)
+        kp = _oracle_keep(w)
+        hs = list(range(w.heads)) if nh is None else [int(x) for x in
+                                                     np.linspace(0, w.heads - 1, nh).round()]
+        f, sec = _oracle_sample(w, kp, layer, batches, hs, with_scas=scas)
+        full = sum(pass_flops(w, kp, lenb_table(kp, w.scale_tokens)).values())
+        whole = len(batches) * len(hs) == w.batch * w.heads and w.layers == 1
+        per[key] = {"workload": w.name, "sample": f"layer {layer}, batch entries {batches}, heads "
+                                                  f"{hs[0]}..{hs[-1]} ({len(hs)} of {w.heads}), all "
+                                                  f"{w.n_scales} scales" + (", S-CAS" if scas else ""),
+                    "sample_seconds": round(sec, 3), "sample_tflop": round(f / 1e12, 5),
+                    "TFLOP_per_s": round(f / sec / 1e12, 5),
+                    "seconds_per_pass": round(sec * full / f, 2),
+                    "seconds_per_pass_is": "measured" if whole else
+                    "extrapolated by algorithmic flops from the sample",
+                    "pass_tflop": round(full / 1e12, 3)}
+    out["per_workload"] = per
+    return out
 
 
 if __name__ == "__main__":

@@ -274,3 +274,33 @@ def test_scale_window_policy_bf16(mode):
     if table is not None:
         _check_scas(wl, exp, inputs, table, [0, 1, 2])
     ctx.close()
+
+
+def test_scale_window_policy_infinity2b_shape():
+    """The window schedule at the shape the benchmark runs it: 32 layers x 16
+    heads, batch 8, two condensed scales, a window of two local scales, the
+    four least similar layers keeping every scale.  A cache-demanding layer
+    and a windowed one are driven end to end with the fused call and checked
+    against the oracle (outputs on sampled rows of three batch entries, the
+    cache of every head after the last two scales); every other layer's
+    region keeps its sentinel."""
+    wl = workloads.get("c2")
+    K, L = wl.n_scales, wl.layers
+    sim = np.random.default_rng(5).random(L).astype(np.float32)
+    exp = hk.build_scale_window_schedule(L, wl.heads, wl.scale_tokens, 2, 2, K, sim, 4)
+    np.testing.assert_array_equal(exp, opol.scale_window_schedule(L, wl.heads, wl.scale_tokens, 2, 2,
+                                                                  K, sim, 4))
+    demanding = int(np.argsort(sim)[0])
+    windowed = int(np.argsort(sim)[-1])
+    assert (exp[demanding] == K - 1).sum() > (exp[windowed] == K - 1).sum()
+    layers = sorted({demanding, windowed})
+    assert _mid_drops(exp[windowed:windowed + 1]) > 0
+    ctx, inputs, outs, _ = _drive(wl, exp, "fused", layers=layers, check_every_step=False)
+    _check_outputs(wl, exp, inputs, outs, layers, rows_per_unit=12, batches=(0, 4, wl.batch - 1))
+    other = [l for l in range(L) if l not in layers][:2]
+    for l in other:
+        lo = int(ctx.base[l, 0])
+        hi = int(ctx.base[l, -1]) + wl.batch * int(ctx.cap[l, -1]) * wl.head_dim
+        for c in (ctx.k_cache, ctx.v_cache):
+            assert (to_host_bits(c[lo:hi]) == SENTINEL_BF16).all(), l
+    ctx.close()

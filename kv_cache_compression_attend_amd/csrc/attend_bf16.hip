@@ -73,10 +73,15 @@
 //     the fragment two slots ahead, one MFMA, one exponential and its share of
 //     the packing and sum) fenced by scheduling barriers, so LDS latency hides
 //     behind the MFMA before it and the exponentials fill the MFMA shadow.
-//     K tiles are staged one tile ahead of V tiles (waves 4-7 load K, waves
-//     0-3 load V) in three LDS buffers each, one barrier per 64 keys.  The
-//     first and last tiles are separate instantiations, so the steady-state
-//     step is straight-line code.
+//     Tiles go from memory straight into LDS (buffer loads with the LDS
+//     flag; waves 4-7 load K, waves 0-3 load V), two tiles ahead of their
+//     use in four LDS buffers each (one ahead in three with S-CAS, whose
+//     sums take the room of the fourth); V stays row-major and the value
+//     product reads its transposed fragments with the CDNA4 transposing LDS
+//     read.  One barrier per 64 keys.  Pooled caches, whose rows are found
+//     through a map, stage through registers instead (V transposed on the
+//     way into LDS).  The first and last tiles are separate instantiations,
+//     so the steady-state step is straight-line code.
 #include <math.h>
 
 #include <algorithm>
@@ -113,6 +118,9 @@ constexpr float kFastTrigger = 1.8446744e19f;  // 2^kFastRange
 // twice the bf16 parity bar, so larger scales keep the exact Q.
 constexpr float kPreMaxScale = 2.f;
 constexpr unsigned kOutOfRange = 0x80000000u;
+// s_waitcnt operand: vector memory count 0 and LDS count 0 (export count
+// not waited on); or'ed with k, vector memory count k.
+constexpr unsigned kWaitVmLds = 0x0070u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
 
@@ -252,6 +260,152 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
     *reinterpret_cast<uint2*>(&sV[d * VSTR + 4 * g]) = even;
     *reinterpret_cast<uint2*>(&sV[(d + 1) * VSTR + 4 * g]) = odd;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Direct staging (256-query tiling, caches with per-head contiguous rows):
+// tiles go from memory straight into LDS (buffer loads with the LDS flag:
+// lane l of a wave's load writes its 16 bytes at the load's LDS base + 16 l;
+// a lane whose offset is out of range writes zeros), with no pass through
+// registers.  A wave's load fills 1 KB of a tile's LDS buffer, i.e. 64
+// consecutive 16-byte chunk slots; a tile row occupies CH slots, of which
+// the first 16 hold the row's 256 bytes and the rest are padding (read out
+// of range).  K rows keep the 272-byte stride of the score product's
+// fragment reads (CH = 17); V stays row-major (keys x dims) with a 320-byte
+// stride (CH = 20), which the transposing LDS reads of the value product
+// take without bank conflicts.
+// ---------------------------------------------------------------------------
+constexpr int VROW = D + 32;               // row-major V tile row stride (bf16 elements)
+constexpr int kKChunks = KSTR / 8;         // 17
+constexpr int kVChunks = VROW / 8;         // 20
+constexpr int kKLoads = BN * kKChunks / 64;  // 17 wave loads per K tile
+constexpr int kVLoads = BN * kVChunks / 64;  // 20 per V tile
+static_assert(BN * kKChunks % 64 == 0 && BN * kVChunks % 64 == 0, "whole wave loads per tile");
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+
+// Waits until at most keep (0..7) of this wave's vector memory operations
+// are outstanding and all of its LDS operations are done.
+__device__ __forceinline__ void wait_vm_keep(int keep) {
+  switch (keep) {
+    case 0: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 0); break;
+    case 1: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 1); break;
+    case 2: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 2); break;
+    case 3: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 3); break;
+    case 4: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 4); break;
+    case 5: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 5); break;
+    case 6: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 6); break;
+    default: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 7); break;
+  }
+}
+
+// Workgroup barrier that does not itself wait for this wave's outstanding
+// direct loads (the callers wait for the ones the next step reads with
+// wait_vm_keep first); the empty asm statements keep the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, unsigned voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, int(voff), 0, 0, 0);
+}
+
+// One wave's share of a tile's direct loads (the four waves of a stager
+// group take loads i = w, w + 4, ...): for its m-th load, this lane's byte
+// offsets in a 64-row block of the cache (rows kRowBytes apart) and of the
+// current scale (rows tokb apart), or kOutOfRange for a padding slot.
+struct DmaLane {
+  unsigned vc[5], vu[5];
+  int w, n;  // first load index, loads of this wave (wave-uniform)
+};
+
+template <int CH, int NLOADS>
+__device__ __forceinline__ DmaLane dma_lane(int w, int lane, int tokb) {
+  DmaLane d;
+  d.w = w;
+  d.n = (NLOADS - w + 3) / 4;
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const int i = w + 4 * m;
+    const int q = 64 * i + lane, row = q / CH, c = q % CH;
+    const bool ok = i < NLOADS && c < 16;
+    d.vc[m] = ok ? unsigned(row * kRowBytes + 16 * c) : kOutOfRange;
+    d.vu[m] = ok ? unsigned(row) * unsigned(tokb) + 16u * c : kOutOfRange;
+  }
+  return d;
+}
+
+// Issues this wave's loads of the tile at key k0 into the LDS buffer buf.
+// Rows past the end of the keys are read as zeros.
+__device__ __forceinline__ void dma_tile(const KeySource& s, int k0, const uint16_t* buf,
+                                         const DmaLane& d) {
+  const char* const lds = reinterpret_cast<const char*>(buf);
+  if (k0 + BN <= s.Lc) {  // all rows in the cache
+    const auto r = rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+      if (m < d.n) dma16(r, lds + 1024 * (d.w + 4 * m), d.vc[m]);
+  } else if (k0 >= s.Lc) {  // all rows in the current scale
+    const int64_t q0 = k0 - s.Lc;
+    const auto r = rsrc(s.cur + q0 * s.tokb, int64_t(s.n - q0 - 1) * s.tokb + kRowBytes);
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+      if (m < d.n) dma16(r, lds + 1024 * (d.w + 4 * m), d.vu[m]);
+  } else {  // junction: rows below split from the cache, the rest from the current scale
+    const int split = s.Lc - k0;
+    const auto rc = rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
+    const auto ru = rsrc(s.cur - int64_t(split) * s.tokb, int64_t(split + s.n - 1) * s.tokb + kRowBytes);
+#pragma unroll
+    for (int m = 0; m < 5; ++m) {
+      if (m < d.n) {
+        // Padding slots (kOutOfRange) take the second branch and read zeros.
+        if (int(d.vc[m] >> 8) < split) dma16(rc, lds + 1024 * (d.w + 4 * m), d.vc[m]);
+        else dma16(ru, lds + 1024 * (d.w + 4 * m), d.vu[m]);
+      }
+    }
+  }
+}
+
+// Fused append with direct staging: the 256 lanes of a stager group copy the
+// rows of the staged tile at key k0 (LDS row stride RS bytes) that belong to
+// the current scale into the cache rows of the same keys.
+template <int RS>
+__device__ __forceinline__ void append_from_lds(const KeySource& s, char* cache, int k0,
+                                                const uint16_t* buf, int l) {
+  if (k0 + BN <= s.Lc) return;
+  const int c = l & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (l >> 4) + 16 * i, key = k0 + row;
+    if (key >= s.Lc && key < s.Ltot)
+      *reinterpret_cast<u32x4*>(cache + int64_t(key) * kRowBytes + 16 * c) =
+          *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(buf) + row * RS + 16 * c);
+  }
+}
+
+// A-operand fragment of the value product from a row-major V tile: dims
+// 32 db + (lane mod 32), keys 16 st + 8 (lane / 32) + 0..7, as two
+// transposing reads of four keys.  Within each 16-lane group the read hands
+// lane i element (i mod 4) of the row addressed by lane 4 r + i / 4, for
+// r = 0..3; lane a of group g therefore addresses key row
+// 8 (g / 2) + a / 4 (+ 4 for the second read) at dims
+// 32 db + 16 (g mod 2) + 4 (a mod 4) .. + 3.  voff: that byte offset for
+// st = db = 0.
+__device__ __forceinline__ int vtr_lane_offset(int lane) {
+  const int g = lane >> 4, a = lane & 15;
+  return (8 * (g >> 1) + (a >> 2)) * VROW * 2 + 32 * (g & 1) + 8 * (a & 3);
+}
+__device__ __forceinline__ u32x4 vfrag_tr(const uint16_t* Vt, int voff, int st, int db) {
+  const char* p = reinterpret_cast<const char*>(Vt) + voff + st * 16 * VROW * 2 + db * 64;
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p));
+  const v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(p + 4 * VROW * 2));
+  const uint2 xa = __builtin_bit_cast(uint2, x), ya = __builtin_bit_cast(uint2, y);
+  return u32x4{xa.x, xa.y, ya.x, ya.y};
 }
 
 // Fused append: the 16-byte chunks held in reg (rows r0 + rstep * i, chunk c
@@ -711,10 +865,17 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // instantiation, so the unsplit kernel carries no split code.
 // PRE (never with S-CAS): Q scaled by alpha * log2 e and rounded to bf16,
 // with the fast mode; only for alpha * log2 e <= kPreMaxScale.
+// Contiguous caches stage their tiles directly into LDS (V row-major);
+// pooled ones (PAGED) through registers (V transposed on the way).
 template <bool SCAS, bool SPLIT, bool PAGED, bool PRE>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[3][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[3][D * VSTR];
+  constexpr bool DIRECT = !PAGED;
+  // LDS buffers per operand, and how many tiles ahead of its first use the
+  // direct staging loads a tile (the S-CAS sums leave room for three).
+  constexpr int NBUF = DIRECT && !SCAS ? 4 : 3;
+  constexpr int PD = NBUF - 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][BN * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][DIRECT ? BN * VROW : D * VSTR];
   __shared__ float sRed[SCAS ? 8 * kMaxScales : 1];
   __shared__ float sScas[SCAS ? kMaxScales * 512 : 1];
 
@@ -722,7 +883,9 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
-  const bool kstager = tid >= 256;
+  // Waves 4-7 stage K, waves 0-3 V (wave-uniform; read as a scalar where
+  // the direct loads need their count to be one).
+  const bool kstager = DIRECT ? __builtin_amdgcn_readfirstlane(tid) >= 256 : tid >= 256;
   const int stid = tid & 255;
   const int qrow = hd.qt * 256 + wave * 32 + j;
   Vec16 qf[8];
@@ -779,14 +942,28 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf.b, qf[kk].b, s, 0, 0, 0);
     }
   };
+  // This lane's share of the direct loads: K by waves 4-7, V by waves 0-3.
+  const int stw = __builtin_amdgcn_readfirstlane(wave) & 3;
+  DmaLane dma;
+  if constexpr (DIRECT) {
+    if (kstager) dma = dma_lane<kKChunks, kKLoads>(stw, lane, hd.tokb);
+    else dma = dma_lane<kVChunks, kVLoads>(stw, lane, hd.tokb);
+  }
+  const int voff = DIRECT ? vtr_lane_offset(lane) : 0;
+  // V^T fragment (dims 32 db + j, keys 16 st + 8 hf + 0..7) of a staged V tile.
+  auto vfrag = [&](const uint16_t* Vt, int st, int db) {
+    Vec16 vf;
+    if constexpr (DIRECT) vf.u = vfrag_tr(Vt, voff, st, db);
+    else vf.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * st + 8 * hf]);
+    return vf;
+  };
   auto pv = [&](const uint16_t* Vt, int kb, const Vec16 (&p)[2]) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int st = 2 * kb + half;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        Vec16 vf;
-        vf.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * st + 8 * hf]);
+        const Vec16 vf = vfrag(Vt, st, db);
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf.b, p[half].b, o[db], 0, 0, 0);
       }
     }
@@ -869,7 +1046,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       Vec16 f;
       if (i < 8) {
         const int half = i >> 2, db = i & 3;
-        f.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * (2 * kbv + half) + 8 * hf]);
+        f = vfrag(Vt, 2 * kbv + half, db);
       } else {
         f.u = *reinterpret_cast<const u32x4*>(kp + 16 * (i - 8));
       }
@@ -928,15 +1105,44 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // workgroup; kept uniform (updated outside the stager branches) so that it
   // stays in a scalar register.
   int next_append = first_append_tile(a, hd, t_lo);
-  if (kstager) {
-    load_k<PAGED>(hd.ks, k_lo, stid, reg);
-    store_k(sK[0], stid, reg);
-    if (hd.append && t_lo == next_append) append_rows<PAGED>(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
-    if (t_lo + 1 < t_hi) load_k<PAGED>(hd.ks, k_lo + BN, stid, reg);
+  // Vector memory operations this wave issued after the previous barrier
+  // that the next one need not wait for (direct staging), or -1: wait for
+  // all of them.
+  int in_flight = 0;
+  if constexpr (DIRECT) {
+    // Direct staging: K(t_lo), K(t_lo + 1) and V(t_lo) straight into LDS,
+    // then (two-tile lead) K(t_lo + 2) and V(t_lo + 1) after the barrier.
+    if (kstager) {
+      dma_tile(hd.ks, k_lo, sK[0], dma);
+      if (t_lo + 1 < t_hi) dma_tile(hd.ks, k_lo + BN, sK[1], dma);
+    } else {
+      dma_tile(hd.vs, k_lo, sV[0], dma);
+    }
+    wait_vm_keep(0);
+    barrier_keep_loads();
+    if (kstager && hd.append && t_lo == next_append) {
+      append_from_lds<KSTR * 2>(hd.ks, kc_w, k_lo, sK[0], stid);
+      in_flight = -1;
+    }
+    if constexpr (PD == 2) {
+      const bool issue = kstager ? t_lo + 2 < t_hi : t_lo + 1 < t_hi;
+      if (issue) {
+        if (kstager) dma_tile(hd.ks, k_lo + 2 * BN, sK[2], dma);
+        else dma_tile(hd.vs, k_lo + BN, sV[1], dma);
+        if (in_flight == 0) in_flight = dma.n;
+      }
+    }
   } else {
-    load_v<PAGED>(hd.vs, k_lo, stid, reg);
+    if (kstager) {
+      load_k<PAGED>(hd.ks, k_lo, stid, reg);
+      store_k(sK[0], stid, reg);
+      if (hd.append && t_lo == next_append) append_rows<PAGED>(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
+      if (t_lo + 1 < t_hi) load_k<PAGED>(hd.ks, k_lo + BN, stid, reg);
+    } else {
+      load_v<PAGED>(hd.vs, k_lo, stid, reg);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   qk(sK[0], 0, s0);
   if constexpr (PRE) {
     // The first unit (it always holds a valid key) sets the reference: 0
@@ -961,21 +1167,23 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool FAST = decltype(fast_c)::value;
     const int k0 = t * BN;
-    const int bn = bk == 2 ? 0 : bk + 1;
-    const int bp = bk == 0 ? 2 : bk - 1;
+    const int bn = bk == NBUF - 1 ? 0 : bk + 1;
+    const int bp = bk == 0 ? NBUF - 1 : bk - 1;
     const bool append_v = hd.append && t == next_append;  // V(t)
     if (t == next_append) next_append += a.n_qtiles;
     const bool append_k = hd.append && t + 1 == next_append;  // K(t + 1)
-    if (kstager) {
-      if constexpr (!LAST) {
-        store_k(sK[bn], stid, reg);
-        if (append_k) append_rows<PAGED>(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
+    if constexpr (!DIRECT) {
+      if (kstager) {
+        if constexpr (!LAST) {
+          store_k(sK[bn], stid, reg);
+          if (append_k) append_rows<PAGED>(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
+        }
+        if (t + 2 < t_hi) load_k<PAGED>(hd.ks, k0 + 2 * BN, stid, reg);
+      } else {
+        store_v(sV[bk], stid, reg);
+        if (append_v) append_rows<PAGED>(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
+        if constexpr (!LAST) load_v<PAGED>(hd.vs, k0 + BN, stid, reg);
       }
-      if (t + 2 < t_hi) load_k<PAGED>(hd.ks, k0 + 2 * BN, stid, reg);
-    } else {
-      store_v(sV[bk], stid, reg);
-      if (append_v) append_rows<PAGED>(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
-      if constexpr (!LAST) load_v<PAGED>(hd.vs, k0 + BN, stid, reg);
     }
 
     // step a: unit (t, keys 0..31)
@@ -985,7 +1193,39 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
     else settle(s0, p0, e0);
     if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
-    __syncthreads();
+    if constexpr (DIRECT) {
+      // K(t + 1) and V(t) have landed: each wave waits for its own loads of
+      // them (those issued PD tiles back; the previous tile's may still be in
+      // flight) and the barrier publishes them.  Then the loads of
+      // K(t + 1 + PD) and V(t + PD), into the buffers that K(t - 1) and
+      // V(t - 2) leave (both last read in step a of the previous tile).
+      wait_vm_keep(in_flight < 0 ? 0 : in_flight);
+      barrier_keep_loads();
+      in_flight = 0;
+      bool stored = false;
+      if (kstager) {
+        if (append_k && t + 1 < t_hi) {
+          append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + BN, sK[bn], stid);
+          stored = true;
+        }
+        if (t + 1 + PD < t_hi) {
+          dma_tile(hd.ks, k0 + (1 + PD) * BN, sK[(bk + 1 + PD) % NBUF], dma);
+          in_flight = dma.n;
+        }
+      } else {
+        if (append_v) {
+          append_from_lds<VROW * 2>(hd.vs, vc_w, k0, sV[bk], stid);
+          stored = true;
+        }
+        if (t + PD < t_hi) {
+          dma_tile(hd.vs, k0 + PD * BN, sV[(bk + PD) % NBUF], dma);
+          in_flight = dma.n;
+        }
+      }
+      if (stored || PD == 1) in_flight = -1;
+    } else {
+      __syncthreads();
+    }
 
     // step b: unit (t, keys 32..63)
     if constexpr (LAST) mask_tail(s1, k0 + 32);
@@ -1013,7 +1253,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     for (; t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, F_{});
     tile(t_hi - 1, F_{}, T_{}, F_{});
   }
-  pv(sV[bk == 0 ? 2 : bk - 1], 1, p1);
+  pv(sV[bk == 0 ? NBUF - 1 : bk - 1], 1, p1);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if constexpr (SPLIT) {

@@ -980,6 +980,10 @@ def compact_rate(args, hk, workloads, torch, np, dev, stream):
     times = {t: [] for t in range(K - 1)}
     for rep in range(4):
         ctx.reset()
+        # The spin kernel holds the GPU while the host queues the pass, so the
+        # events time the launches, not the host's calls between them (the
+        # early scales move a few MB and would otherwise wait on the host).
+        gpu_sleep(torch)
         for t in range(K - 1):
             ev[t][0].record(stream)
             ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)

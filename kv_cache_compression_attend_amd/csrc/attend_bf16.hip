@@ -1090,14 +1090,17 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     return psum + l1;
   };
 
-  u32x4 reg[4];  // K(t+2) on waves 4-7, V(t+1) on waves 0-3
+  // Register staging (pooled caches only): K(t + 2) on waves 4-7, V(t + 1)
+  // on waves 0-3.
+  u32x4 reg[4];
   f32x16 s0, s1;
   Vec16 p0[2], p1[2];
 #pragma unroll
   for (int half = 0; half < 2; ++half) p1[half].u = u32x4{0, 0, 0, 0};
 
-  // Prologue: K(t_lo) in buffer 0; K(t_lo + 1) (waves 4-7) and V(t_lo)
-  // (waves 0-3) in registers.  Every split holds at least one tile.
+  // Prologue: K(t_lo) in buffer 0; with register staging K(t_lo + 1)
+  // (waves 4-7) and V(t_lo) (waves 0-3) in registers, with direct staging
+  // in their LDS buffers.  Every split holds at least one tile.
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
   const int k_lo = t_lo * BN;

@@ -1112,28 +1112,27 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // that the next one need not wait for (direct staging), or -1: wait for
   // all of them.
   int in_flight = 0;
+  // Whether this workgroup writes key tile x of the current scale into the
+  // cache (fused append: tile x falls to the q-tile x mod n_qtiles).
+  auto owns = [&](int x) { return hd.append && x % a.n_qtiles == hd.qt; };
   if constexpr (DIRECT) {
-    // Direct staging: K(t_lo), K(t_lo + 1) and V(t_lo) straight into LDS,
-    // then (two-tile lead) K(t_lo + 2) and V(t_lo + 1) after the barrier.
+    // Direct staging: K(t_lo) and V(t_lo) straight into LDS, with K(t_lo + 1)
+    // (one-tile lead, S-CAS) or K(t_lo + 1), K(t_lo + 2) and V(t_lo + 1)
+    // (paired tiles: the loads of two tiles are published by one barrier).
     if (kstager) {
-      dma_tile(hd.ks, k_lo, sK[0], dma);
-      if (t_lo + 1 < t_hi) dma_tile(hd.ks, k_lo + BN, sK[1], dma);
+#pragma unroll
+      for (int x = 0; x <= PD; ++x)
+        if (t_lo + x < t_hi) dma_tile(hd.ks, k_lo + x * BN, sK[x], dma);
     } else {
-      dma_tile(hd.vs, k_lo, sV[0], dma);
+#pragma unroll
+      for (int x = 0; x < PD; ++x)
+        if (t_lo + x < t_hi) dma_tile(hd.vs, k_lo + x * BN, sV[x], dma);
     }
     wait_vm_keep(0);
     barrier_keep_loads();
-    if (kstager && hd.append && t_lo == next_append) {
+    if (kstager && owns(t_lo)) {
       append_from_lds<KSTR * 2>(hd.ks, kc_w, k_lo, sK[0], stid);
       in_flight = -1;
-    }
-    if constexpr (PD == 2) {
-      const bool issue = kstager ? t_lo + 2 < t_hi : t_lo + 1 < t_hi;
-      if (issue) {
-        if (kstager) dma_tile(hd.ks, k_lo + 2 * BN, sK[2], dma);
-        else dma_tile(hd.vs, k_lo + BN, sV[1], dma);
-        if (in_flight == 0) in_flight = dma.n;
-      }
     }
   } else {
     if (kstager) {
@@ -1196,12 +1195,42 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
     else settle(s0, p0, e0);
     if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
-    if constexpr (DIRECT) {
-      // K(t + 1) and V(t) have landed: each wave waits for its own loads of
-      // them (those issued PD tiles back; the previous tile's may still be in
-      // flight) and the barrier publishes them.  Then the loads of
-      // K(t + 1 + PD) and V(t + PD), into the buffers that K(t - 1) and
-      // V(t - 2) leave (both last read in step a of the previous tile).
+    if constexpr (DIRECT && PD == 2) {
+      // Paired tiles, one barrier every second tile (t - t_lo even).  By the
+      // barrier of tile t, K(t + 1), K(t + 2), V(t) and V(t + 1) have landed
+      // (loaded at the barrier two tiles back, or in the prologue; each wave
+      // waits for its own loads, the barrier publishes them): steps b(t),
+      // a(t + 1), b(t + 1) and a(t + 2) read nothing else.  Then the appends
+      // of those tiles that fall to this workgroup, and the loads of
+      // K(t + 3), K(t + 4), V(t + 2) and V(t + 3) into the buffers of K(t - 1),
+      // K(t), V(t - 2) and V(t - 1), each last read in step a of tile t at
+      // the latest.
+      if (((t - t_lo) & 1) == 0) {
+        wait_vm_keep(0);
+        barrier_keep_loads();
+        if (kstager) {
+#pragma unroll
+          for (int x = 1; x <= 2; ++x)
+            if (t + x < t_hi && owns(t + x))
+              append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + x * BN, sK[(bk + x) % NBUF], stid);
+#pragma unroll
+          for (int x = 3; x <= 4; ++x)
+            if (t + x < t_hi) dma_tile(hd.ks, k0 + x * BN, sK[(bk + x) % NBUF], dma);
+        } else {
+#pragma unroll
+          for (int x = 0; x <= 1; ++x)
+            if (t + x < t_hi && owns(t + x))
+              append_from_lds<VROW * 2>(hd.vs, vc_w, k0 + x * BN, sV[(bk + x) % NBUF], stid);
+#pragma unroll
+          for (int x = 2; x <= 3; ++x)
+            if (t + x < t_hi) dma_tile(hd.vs, k0 + x * BN, sV[(bk + x) % NBUF], dma);
+        }
+      }
+    } else if constexpr (DIRECT) {
+      // One tile ahead (S-CAS): K(t + 1) and V(t) have landed (each wave
+      // waits for its own loads; the barrier publishes them).  Then the loads
+      // of K(t + 2) and V(t + 1), into the buffers that K(t - 1) and V(t - 2)
+      // leave (both last read in step a of the previous tile).
       wait_vm_keep(in_flight < 0 ? 0 : in_flight);
       barrier_keep_loads();
       in_flight = 0;

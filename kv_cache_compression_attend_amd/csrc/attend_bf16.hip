@@ -74,14 +74,17 @@
 //     the packing and sum) fenced by scheduling barriers, so LDS latency hides
 //     behind the MFMA before it and the exponentials fill the MFMA shadow.
 //     Tiles go from memory straight into LDS (buffer loads with the LDS
-//     flag; waves 4-7 load K, waves 0-3 load V), two tiles ahead of their
-//     use in four LDS buffers each (one ahead in three with S-CAS, whose
-//     sums take the room of the fourth); V stays row-major and the value
-//     product reads its transposed fragments with the CDNA4 transposing LDS
-//     read.  One barrier per 64 keys.  Pooled caches, whose rows are found
-//     through a map, stage through registers instead (V transposed on the
-//     way into LDS).  The first and last tiles are separate instantiations,
-//     so the steady-state step is straight-line code.
+//     flag; waves 4-7 load K, waves 0-3 load V) in four LDS buffers per
+//     operand, in pairs: one barrier per two 64-key tiles publishes the next
+//     two tiles of K and V, the K waves load two tiles at that barrier and
+//     the V waves two at the start of the following tile.  With S-CAS, whose
+//     sums take the room of the fourth buffer, three buffers, a tile ahead,
+//     one barrier per tile.  V stays row-major and the value product reads
+//     its transposed fragments with the CDNA4 transposing LDS read.  Pooled
+//     caches, whose rows are found through a map, stage through registers
+//     instead (V transposed on the way into LDS, one barrier per tile).  The
+//     first and last tiles are separate instantiations, so the steady-state
+//     step is straight-line code.
 #include <math.h>
 
 #include <algorithm>
@@ -1188,6 +1191,19 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       }
     }
 
+    if constexpr (DIRECT && PD == 2) {
+      // Paired tiles, odd tile t (no barrier): the V-staging waves load
+      // V(t + 1) and V(t + 2) into the buffers of V(t - 3) and V(t - 2), both
+      // last read in step a of tile t - 1, before the previous barrier.  The
+      // K-staging waves load at the even tiles' barriers, so the two waves of
+      // a SIMD never issue their loads at the same time (measured: 6% fewer
+      // cycles than both at the barrier).
+      if (((t - t_lo) & 1) == 1 && !kstager) {
+#pragma unroll
+        for (int x = 1; x <= 2; ++x)
+          if (t + x < t_hi) dma_tile(hd.vs, k0 + x * BN, sV[(bk + x) % NBUF], dma);
+      }
+    }
     // step a: unit (t, keys 0..31)
     if constexpr (LAST) mask_tail(s0, k0);
     float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
@@ -1198,13 +1214,12 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if constexpr (DIRECT && PD == 2) {
       // Paired tiles, one barrier every second tile (t - t_lo even).  By the
       // barrier of tile t, K(t + 1), K(t + 2), V(t) and V(t + 1) have landed
-      // (loaded at the barrier two tiles back, or in the prologue; each wave
-      // waits for its own loads, the barrier publishes them): steps b(t),
-      // a(t + 1), b(t + 1) and a(t + 2) read nothing else.  Then the appends
-      // of those tiles that fall to this workgroup, and the loads of
-      // K(t + 3), K(t + 4), V(t + 2) and V(t + 3) into the buffers of K(t - 1),
-      // K(t), V(t - 2) and V(t - 1), each last read in step a of tile t at
-      // the latest.
+      // (loaded two tiles back, or in the prologue; each wave waits for its
+      // own loads, the barrier publishes them): steps b(t), a(t + 1), b(t + 1)
+      // and a(t + 2) read nothing else.  Then the appends of those tiles that
+      // fall to this workgroup, and the K-staging waves' loads of K(t + 3) and
+      // K(t + 4) into the buffers of K(t - 1) and K(t), both last read in step
+      // a of tile t at the latest (V: at the start of tile t + 1).
       if (((t - t_lo) & 1) == 0) {
         wait_vm_keep(0);
         barrier_keep_loads();
@@ -1221,9 +1236,6 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
           for (int x = 0; x <= 1; ++x)
             if (t + x < t_hi && owns(t + x))
               append_from_lds<VROW * 2>(hd.vs, vc_w, k0 + x * BN, sV[(bk + x) % NBUF], stid);
-#pragma unroll
-          for (int x = 2; x <= 3; ++x)
-            if (t + x < t_hi) dma_tile(hd.vs, k0 + x * BN, sV[(bk + x) % NBUF], dma);
         }
       }
     } else if constexpr (DIRECT) {

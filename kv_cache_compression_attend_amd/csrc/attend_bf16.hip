@@ -343,16 +343,41 @@ __device__ __forceinline__ DmaLane dma_lane(int w, int lane, int tokb) {
   return d;
 }
 
+// Pooled caches: the pool row of the row each of this wave's loads of the
+// tile at key x0 takes from the cache (0 for rows past the held ones, which
+// come from the current scale, and for padding slots), read from the map one
+// burst of loads ahead of its use.
+__device__ __forceinline__ void map_prefetch(const KeySource& s, int x0, const DmaLane& d,
+                                             unsigned (&mv)[5]) {
+  const int held = min(s.Lc - x0, BN);
+  if (held <= 0) return;
+  const auto r = rsrc(s.map + x0, int64_t(held) * 4);
+#pragma unroll
+  for (int m = 0; m < 5; ++m)
+    if (m < d.n) mv[m] = __builtin_amdgcn_raw_buffer_load_b32(r, int((d.vc[m] >> 8) * 4u), 0, 0);
+}
+
 // Issues this wave's loads of the tile at key k0 into the LDS buffer buf.
-// Rows past the end of the keys are read as zeros.
+// Rows past the end of the keys are read as zeros.  PAGED: cache rows come
+// from the pool rows in mv (map_prefetch of the same tile).
+template <bool PAGED>
 __device__ __forceinline__ void dma_tile(const KeySource& s, int k0, const uint16_t* buf,
-                                         const DmaLane& d) {
+                                         const DmaLane& d, const unsigned (&mv)[5]) {
   const char* const lds = reinterpret_cast<const char*>(buf);
+  // Byte offset of the cache part of load m: the pool row's, or the row's
+  // within the tile's contiguous block.
+  auto coff = [&](int m) {
+    if constexpr (PAGED)
+      return d.vc[m] == kOutOfRange ? kOutOfRange : mv[m] * unsigned(kRowBytes) + (d.vc[m] & 255u);
+    else
+      return d.vc[m];
+  };
   if (k0 + BN <= s.Lc) {  // all rows in the cache
-    const auto r = rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
+    const auto r = PAGED ? rsrc(s.cache, s.pool_bytes)
+                         : rsrc(s.cache + int64_t(k0) * kRowBytes, BN * kRowBytes);
 #pragma unroll
     for (int m = 0; m < 5; ++m)
-      if (m < d.n) dma16(r, lds + 1024 * (d.w + 4 * m), d.vc[m]);
+      if (m < d.n) dma16(r, lds + 1024 * (d.w + 4 * m), coff(m));
   } else if (k0 >= s.Lc) {  // all rows in the current scale
     const int64_t q0 = k0 - s.Lc;
     const auto r = rsrc(s.cur + q0 * s.tokb, int64_t(s.n - q0 - 1) * s.tokb + kRowBytes);
@@ -361,13 +386,14 @@ __device__ __forceinline__ void dma_tile(const KeySource& s, int k0, const uint1
       if (m < d.n) dma16(r, lds + 1024 * (d.w + 4 * m), d.vu[m]);
   } else {  // junction: rows below split from the cache, the rest from the current scale
     const int split = s.Lc - k0;
-    const auto rc = rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
+    const auto rc = PAGED ? rsrc(s.cache, s.pool_bytes)
+                          : rsrc(s.cache + int64_t(k0) * kRowBytes, int64_t(split) * kRowBytes);
     const auto ru = rsrc(s.cur - int64_t(split) * s.tokb, int64_t(split + s.n - 1) * s.tokb + kRowBytes);
 #pragma unroll
     for (int m = 0; m < 5; ++m) {
       if (m < d.n) {
         // Padding slots (kOutOfRange) take the second branch and read zeros.
-        if (int(d.vc[m] >> 8) < split) dma16(rc, lds + 1024 * (d.w + 4 * m), d.vc[m]);
+        if (int(d.vc[m] >> 8) < split) dma16(rc, lds + 1024 * (d.w + 4 * m), coff(m));
         else dma16(ru, lds + 1024 * (d.w + 4 * m), d.vu[m]);
       }
     }
@@ -872,7 +898,7 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // pooled ones (PAGED) through registers (V transposed on the way).
 template <bool SCAS, bool SPLIT, bool PAGED, bool PRE>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
-  constexpr bool DIRECT = !PAGED;
+  constexpr bool DIRECT = true;
   // LDS buffers per operand, and how many tiles ahead of its first use the
   // direct staging loads a tile (the S-CAS sums leave room for three).
   constexpr int NBUF = DIRECT && !SCAS ? 4 : 3;
@@ -948,6 +974,9 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // This lane's share of the direct loads: K by waves 4-7, V by waves 0-3.
   const int stw = __builtin_amdgcn_readfirstlane(wave) & 3;
   DmaLane dma;
+  // Pooled caches: pool rows of the rows this wave loads in its next burst
+  // (one tile, or two with paired tiles).
+  unsigned mv[2][5];
   if constexpr (DIRECT) {
     if (kstager) dma = dma_lane<kKChunks, kKLoads>(stw, lane, hd.tokb);
     else dma = dma_lane<kVChunks, kVLoads>(stw, lane, hd.tokb);
@@ -1122,14 +1151,32 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     // Direct staging: K(t_lo) and V(t_lo) straight into LDS, with K(t_lo + 1)
     // (one-tile lead, S-CAS) or K(t_lo + 1), K(t_lo + 2) and V(t_lo + 1)
     // (paired tiles: the loads of two tiles are published by one barrier).
+    // Pooled caches read each tile's pool rows first (map_prefetch), the
+    // prologue's tiles one after another and the first burst's ahead.
     if (kstager) {
 #pragma unroll
-      for (int x = 0; x <= PD; ++x)
-        if (t_lo + x < t_hi) dma_tile(hd.ks, k_lo + x * BN, sK[x], dma);
+      for (int x = 0; x <= PD; ++x) {
+        if (t_lo + x < t_hi) {
+          if constexpr (PAGED) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[0]);
+          dma_tile<PAGED>(hd.ks, k_lo + x * BN, sK[x], dma, mv[0]);
+        }
+      }
+      if constexpr (PAGED)
+#pragma unroll
+        for (int x = PD + 1; x <= 2 * PD; ++x)
+          if (t_lo + x < t_hi) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[x - PD - 1]);
     } else {
 #pragma unroll
-      for (int x = 0; x < PD; ++x)
-        if (t_lo + x < t_hi) dma_tile(hd.vs, k_lo + x * BN, sV[x], dma);
+      for (int x = 0; x < PD; ++x) {
+        if (t_lo + x < t_hi) {
+          if constexpr (PAGED) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[0]);
+          dma_tile<PAGED>(hd.vs, k_lo + x * BN, sV[x], dma, mv[0]);
+        }
+      }
+      if constexpr (PAGED)
+#pragma unroll
+        for (int x = PD; x < 2 * PD; ++x)
+          if (t_lo + x < t_hi) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[x - PD]);
     }
     wait_vm_keep(0);
     barrier_keep_loads();
@@ -1201,7 +1248,11 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       if (((t - t_lo) & 1) == 1 && !kstager) {
 #pragma unroll
         for (int x = 1; x <= 2; ++x)
-          if (t + x < t_hi) dma_tile(hd.vs, k0 + x * BN, sV[(bk + x) % NBUF], dma);
+          if (t + x < t_hi) dma_tile<PAGED>(hd.vs, k0 + x * BN, sV[(bk + x) % NBUF], dma, mv[x - 1]);
+        if constexpr (PAGED)
+#pragma unroll
+          for (int x = 3; x <= 4; ++x)
+            if (t + x < t_hi) map_prefetch(hd.vs, k0 + x * BN, dma, mv[x - 3]);
       }
     }
     // step a: unit (t, keys 0..31)
@@ -1230,7 +1281,11 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
               append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + x * BN, sK[(bk + x) % NBUF], stid);
 #pragma unroll
           for (int x = 3; x <= 4; ++x)
-            if (t + x < t_hi) dma_tile(hd.ks, k0 + x * BN, sK[(bk + x) % NBUF], dma);
+            if (t + x < t_hi) dma_tile<PAGED>(hd.ks, k0 + x * BN, sK[(bk + x) % NBUF], dma, mv[x - 3]);
+          if constexpr (PAGED)
+#pragma unroll
+            for (int x = 5; x <= 6; ++x)
+              if (t + x < t_hi) map_prefetch(hd.ks, k0 + x * BN, dma, mv[x - 5]);
         } else {
 #pragma unroll
           for (int x = 0; x <= 1; ++x)
@@ -1253,18 +1308,22 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
           stored = true;
         }
         if (t + 1 + PD < t_hi) {
-          dma_tile(hd.ks, k0 + (1 + PD) * BN, sK[(bk + 1 + PD) % NBUF], dma);
+          dma_tile<PAGED>(hd.ks, k0 + (1 + PD) * BN, sK[(bk + 1 + PD) % NBUF], dma, mv[0]);
           in_flight = dma.n;
         }
+        if constexpr (PAGED)
+          if (t + 2 + PD < t_hi) map_prefetch(hd.ks, k0 + (2 + PD) * BN, dma, mv[0]);
       } else {
         if (append_v) {
           append_from_lds<VROW * 2>(hd.vs, vc_w, k0, sV[bk], stid);
           stored = true;
         }
         if (t + PD < t_hi) {
-          dma_tile(hd.vs, k0 + PD * BN, sV[(bk + PD) % NBUF], dma);
+          dma_tile<PAGED>(hd.vs, k0 + PD * BN, sV[(bk + PD) % NBUF], dma, mv[0]);
           in_flight = dma.n;
         }
+        if constexpr (PAGED)
+          if (t + 1 + PD < t_hi) map_prefetch(hd.vs, k0 + (1 + PD) * BN, dma, mv[0]);
       }
       if (stored || PD == 1) in_flight = -1;
     } else {

@@ -81,10 +81,10 @@
 //     sums take the room of the fourth buffer, three buffers, a tile ahead,
 //     one barrier per tile.  V stays row-major and the value product reads
 //     its transposed fragments with the CDNA4 transposing LDS read.  Pooled
-//     caches, whose rows are found through a map, stage through registers
-//     instead (V transposed on the way into LDS, one barrier per tile).  The
-//     first and last tiles are separate instantiations, so the steady-state
-//     step is straight-line code.
+//     caches, whose rows are found through a map, read each burst's pool
+//     rows one burst ahead.  The first and last tiles are separate
+//     instantiations, so the steady-state step is straight-line code.  (The
+//     128-query tiling stages through registers, V transposed on the way.)
 #include <math.h>
 
 #include <algorithm>
@@ -122,7 +122,7 @@ constexpr float kFastTrigger = 1.8446744e19f;  // 2^kFastRange
 constexpr float kPreMaxScale = 2.f;
 constexpr unsigned kOutOfRange = 0x80000000u;
 // s_waitcnt operand: vector memory count 0 and LDS count 0 (export count
-// not waited on); or'ed with k, vector memory count k.
+// not waited on).
 constexpr unsigned kWaitVmLds = 0x0070u;
 constexpr int kRsrcFlags = 0x00020000;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;
@@ -266,7 +266,7 @@ __device__ __forceinline__ void store_v(uint16_t* sV, int l, const u32x4 (&reg)[
 }
 
 // ---------------------------------------------------------------------------
-// Direct staging (256-query tiling, caches with per-head contiguous rows):
+// Direct staging (256-query tiling):
 // tiles go from memory straight into LDS (buffer loads with the LDS flag:
 // lane l of a wave's load writes its 16 bytes at the load's LDS base + 16 l;
 // a lane whose offset is out of range writes zeros), with no pass through
@@ -289,25 +289,14 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 
-// Waits until at most keep (0..7) of this wave's vector memory operations
-// are outstanding and all of its LDS operations are done.
-__device__ __forceinline__ void wait_vm_keep(int keep) {
-  switch (keep) {
-    case 0: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 0); break;
-    case 1: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 1); break;
-    case 2: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 2); break;
-    case 3: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 3); break;
-    case 4: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 4); break;
-    case 5: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 5); break;
-    case 6: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 6); break;
-    default: __builtin_amdgcn_s_waitcnt(kWaitVmLds | 7); break;
-  }
-}
+// Waits for all of this wave's vector memory operations (its direct loads
+// included) and LDS operations.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(kWaitVmLds); }
 
 // Workgroup barrier that does not itself wait for this wave's outstanding
-// direct loads (the callers wait for the ones the next step reads with
-// wait_vm_keep first); the empty asm statements keep the compiler from
-// moving memory accesses across it.
+// direct loads (the fenced barrier would; the callers wait with wait_loads
+// where the next steps read what the loads bring); the empty asm statements
+// keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void barrier_keep_loads() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -894,17 +883,16 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // instantiation, so the unsplit kernel carries no split code.
 // PRE (never with S-CAS): Q scaled by alpha * log2 e and rounded to bf16,
 // with the fast mode; only for alpha * log2 e <= kPreMaxScale.
-// Contiguous caches stage their tiles directly into LDS (V row-major);
-// pooled ones (PAGED) through registers (V transposed on the way).
+// PAGED: the cache is a pool whose rows the per-(step, layer, head) map
+// gives (tile loads take per-lane pool offsets).
 template <bool SCAS, bool SPLIT, bool PAGED, bool PRE>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
-  constexpr bool DIRECT = true;
   // LDS buffers per operand, and how many tiles ahead of its first use the
   // direct staging loads a tile (the S-CAS sums leave room for three).
-  constexpr int NBUF = DIRECT && !SCAS ? 4 : 3;
+  constexpr int NBUF = SCAS ? 3 : 4;
   constexpr int PD = NBUF - 2;
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][DIRECT ? BN * VROW : D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][BN * VROW];
   __shared__ float sRed[SCAS ? 8 * kMaxScales : 1];
   __shared__ float sScas[SCAS ? kMaxScales * 512 : 1];
 
@@ -912,9 +900,9 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, hf = lane >> 5;
-  // Waves 4-7 stage K, waves 0-3 V (wave-uniform; read as a scalar where
-  // the direct loads need their count to be one).
-  const bool kstager = DIRECT ? __builtin_amdgcn_readfirstlane(tid) >= 256 : tid >= 256;
+  // Waves 4-7 stage K, waves 0-3 V (wave-uniform, read as a scalar so that
+  // the loads' count is one).
+  const bool kstager = __builtin_amdgcn_readfirstlane(tid) >= 256;
   const int stid = tid & 255;
   const int qrow = hd.qt * 256 + wave * 32 + j;
   Vec16 qf[8];
@@ -977,16 +965,13 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // Pooled caches: pool rows of the rows this wave loads in its next burst
   // (one tile, or two with paired tiles).
   unsigned mv[2][5];
-  if constexpr (DIRECT) {
-    if (kstager) dma = dma_lane<kKChunks, kKLoads>(stw, lane, hd.tokb);
-    else dma = dma_lane<kVChunks, kVLoads>(stw, lane, hd.tokb);
-  }
-  const int voff = DIRECT ? vtr_lane_offset(lane) : 0;
+  if (kstager) dma = dma_lane<kKChunks, kKLoads>(stw, lane, hd.tokb);
+  else dma = dma_lane<kVChunks, kVLoads>(stw, lane, hd.tokb);
+  const int voff = vtr_lane_offset(lane);
   // V^T fragment (dims 32 db + j, keys 16 st + 8 hf + 0..7) of a staged V tile.
   auto vfrag = [&](const uint16_t* Vt, int st, int db) {
     Vec16 vf;
-    if constexpr (DIRECT) vf.u = vfrag_tr(Vt, voff, st, db);
-    else vf.u = *reinterpret_cast<const u32x4*>(&Vt[(32 * db + j) * VSTR + 16 * st + 8 * hf]);
+    vf.u = vfrag_tr(Vt, voff, st, db);
     return vf;
   };
   auto pv = [&](const uint16_t* Vt, int kb, const Vec16 (&p)[2]) {
@@ -1122,9 +1107,6 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     return psum + l1;
   };
 
-  // Register staging (pooled caches only): K(t + 2) on waves 4-7, V(t + 1)
-  // on waves 0-3.
-  u32x4 reg[4];
   f32x16 s0, s1;
   Vec16 p0[2], p1[2];
 #pragma unroll
@@ -1140,61 +1122,42 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // workgroup; kept uniform (updated outside the stager branches) so that it
   // stays in a scalar register.
   int next_append = first_append_tile(a, hd, t_lo);
-  // Vector memory operations this wave issued after the previous barrier
-  // that the next one need not wait for (direct staging), or -1: wait for
-  // all of them.
-  int in_flight = 0;
   // Whether this workgroup writes key tile x of the current scale into the
   // cache (fused append: tile x falls to the q-tile x mod n_qtiles).
   auto owns = [&](int x) { return hd.append && x % a.n_qtiles == hd.qt; };
-  if constexpr (DIRECT) {
-    // Direct staging: K(t_lo) and V(t_lo) straight into LDS, with K(t_lo + 1)
-    // (one-tile lead, S-CAS) or K(t_lo + 1), K(t_lo + 2) and V(t_lo + 1)
-    // (paired tiles: the loads of two tiles are published by one barrier).
-    // Pooled caches read each tile's pool rows first (map_prefetch), the
-    // prologue's tiles one after another and the first burst's ahead.
-    if (kstager) {
+  // Direct staging: K(t_lo) and V(t_lo) straight into LDS, with K(t_lo + 1)
+  // (one-tile lead, S-CAS) or K(t_lo + 1), K(t_lo + 2) and V(t_lo + 1)
+  // (paired tiles: the loads of two tiles are published by one barrier).
+  // Pooled caches read each tile's pool rows first (map_prefetch), the
+  // prologue's tiles one after another and the first burst's ahead.
+  if (kstager) {
 #pragma unroll
-      for (int x = 0; x <= PD; ++x) {
-        if (t_lo + x < t_hi) {
-          if constexpr (PAGED) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[0]);
-          dma_tile<PAGED>(hd.ks, k_lo + x * BN, sK[x], dma, mv[0]);
-        }
+    for (int x = 0; x <= PD; ++x) {
+      if (t_lo + x < t_hi) {
+        if constexpr (PAGED) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[0]);
+        dma_tile<PAGED>(hd.ks, k_lo + x * BN, sK[x], dma, mv[0]);
       }
-      if constexpr (PAGED)
-#pragma unroll
-        for (int x = PD + 1; x <= 2 * PD; ++x)
-          if (t_lo + x < t_hi) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[x - PD - 1]);
-    } else {
-#pragma unroll
-      for (int x = 0; x < PD; ++x) {
-        if (t_lo + x < t_hi) {
-          if constexpr (PAGED) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[0]);
-          dma_tile<PAGED>(hd.vs, k_lo + x * BN, sV[x], dma, mv[0]);
-        }
-      }
-      if constexpr (PAGED)
-#pragma unroll
-        for (int x = PD; x < 2 * PD; ++x)
-          if (t_lo + x < t_hi) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[x - PD]);
     }
-    wait_vm_keep(0);
-    barrier_keep_loads();
-    if (kstager && owns(t_lo)) {
-      append_from_lds<KSTR * 2>(hd.ks, kc_w, k_lo, sK[0], stid);
-      in_flight = -1;
-    }
+    if constexpr (PAGED)
+#pragma unroll
+      for (int x = PD + 1; x <= 2 * PD; ++x)
+        if (t_lo + x < t_hi) map_prefetch(hd.ks, k_lo + x * BN, dma, mv[x - PD - 1]);
   } else {
-    if (kstager) {
-      load_k<PAGED>(hd.ks, k_lo, stid, reg);
-      store_k(sK[0], stid, reg);
-      if (hd.append && t_lo == next_append) append_rows<PAGED>(hd.ks, kc_w, k_lo, stid >> 4, 16, stid & 15, reg);
-      if (t_lo + 1 < t_hi) load_k<PAGED>(hd.ks, k_lo + BN, stid, reg);
-    } else {
-      load_v<PAGED>(hd.vs, k_lo, stid, reg);
+#pragma unroll
+    for (int x = 0; x < PD; ++x) {
+      if (t_lo + x < t_hi) {
+        if constexpr (PAGED) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[0]);
+        dma_tile<PAGED>(hd.vs, k_lo + x * BN, sV[x], dma, mv[0]);
+      }
     }
-    __syncthreads();
+    if constexpr (PAGED)
+#pragma unroll
+      for (int x = PD; x < 2 * PD; ++x)
+        if (t_lo + x < t_hi) map_prefetch(hd.vs, k_lo + x * BN, dma, mv[x - PD]);
   }
+  wait_loads();
+  barrier_keep_loads();
+  if (kstager && owns(t_lo)) append_from_lds<KSTR * 2>(hd.ks, kc_w, k_lo, sK[0], stid);
   qk(sK[0], 0, s0);
   if constexpr (PRE) {
     // The first unit (it always holds a valid key) sets the reference: 0
@@ -1224,21 +1187,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     const bool append_v = hd.append && t == next_append;  // V(t)
     if (t == next_append) next_append += a.n_qtiles;
     const bool append_k = hd.append && t + 1 == next_append;  // K(t + 1)
-    if constexpr (!DIRECT) {
-      if (kstager) {
-        if constexpr (!LAST) {
-          store_k(sK[bn], stid, reg);
-          if (append_k) append_rows<PAGED>(hd.ks, kc_w, k0 + BN, stid >> 4, 16, stid & 15, reg);
-        }
-        if (t + 2 < t_hi) load_k<PAGED>(hd.ks, k0 + 2 * BN, stid, reg);
-      } else {
-        store_v(sV[bk], stid, reg);
-        if (append_v) append_rows<PAGED>(hd.vs, vc_w, k0, 4 * (stid & 15), 1, stid >> 4, reg);
-        if constexpr (!LAST) load_v<PAGED>(hd.vs, k0 + BN, stid, reg);
-      }
-    }
-
-    if constexpr (DIRECT && PD == 2) {
+    if constexpr (PD == 2) {
       // Paired tiles, odd tile t (no barrier): the V-staging waves load
       // V(t + 1) and V(t + 2) into the buffers of V(t - 3) and V(t - 2), both
       // last read in step a of tile t - 1, before the previous barrier.  The
@@ -1262,7 +1211,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
     else settle(s0, p0, e0);
     if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
-    if constexpr (DIRECT && PD == 2) {
+    if constexpr (PD == 2) {
       // Paired tiles, one barrier every second tile (t - t_lo even).  By the
       // barrier of tile t, K(t + 1), K(t + 2), V(t) and V(t + 1) have landed
       // (loaded two tiles back, or in the prologue; each wave waits for its
@@ -1272,7 +1221,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       // K(t + 4) into the buffers of K(t - 1) and K(t), both last read in step
       // a of tile t at the latest (V: at the start of tile t + 1).
       if (((t - t_lo) & 1) == 0) {
-        wait_vm_keep(0);
+        wait_loads();
         barrier_keep_loads();
         if (kstager) {
 #pragma unroll
@@ -1293,41 +1242,25 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
               append_from_lds<VROW * 2>(hd.vs, vc_w, k0 + x * BN, sV[(bk + x) % NBUF], stid);
         }
       }
-    } else if constexpr (DIRECT) {
-      // One tile ahead (S-CAS): K(t + 1) and V(t) have landed (each wave
-      // waits for its own loads; the barrier publishes them).  Then the loads
-      // of K(t + 2) and V(t + 1), into the buffers that K(t - 1) and V(t - 2)
-      // leave (both last read in step a of the previous tile).
-      wait_vm_keep(in_flight < 0 ? 0 : in_flight);
-      barrier_keep_loads();
-      in_flight = 0;
-      bool stored = false;
-      if (kstager) {
-        if (append_k && t + 1 < t_hi) {
-          append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + BN, sK[bn], stid);
-          stored = true;
-        }
-        if (t + 1 + PD < t_hi) {
-          dma_tile<PAGED>(hd.ks, k0 + (1 + PD) * BN, sK[(bk + 1 + PD) % NBUF], dma, mv[0]);
-          in_flight = dma.n;
-        }
-        if constexpr (PAGED)
-          if (t + 2 + PD < t_hi) map_prefetch(hd.ks, k0 + (2 + PD) * BN, dma, mv[0]);
-      } else {
-        if (append_v) {
-          append_from_lds<VROW * 2>(hd.vs, vc_w, k0, sV[bk], stid);
-          stored = true;
-        }
-        if (t + PD < t_hi) {
-          dma_tile<PAGED>(hd.vs, k0 + PD * BN, sV[(bk + PD) % NBUF], dma, mv[0]);
-          in_flight = dma.n;
-        }
-        if constexpr (PAGED)
-          if (t + 1 + PD < t_hi) map_prefetch(hd.vs, k0 + (1 + PD) * BN, dma, mv[0]);
-      }
-      if (stored || PD == 1) in_flight = -1;
     } else {
-      __syncthreads();
+      // One tile ahead (S-CAS): K(t + 1) and V(t) have landed (each wave
+      // waits for its own loads; the barrier publishes them).  Then the
+      // appends, and the loads of K(t + 2) and V(t + 1) into the buffers that
+      // K(t - 1) and V(t - 2) leave (both last read in step a of the previous
+      // tile).
+      wait_loads();
+      barrier_keep_loads();
+      if (kstager) {
+        if (append_k && t + 1 < t_hi) append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + BN, sK[bn], stid);
+        if (t + 2 < t_hi) dma_tile<PAGED>(hd.ks, k0 + 2 * BN, sK[bp], dma, mv[0]);
+        if constexpr (PAGED)
+          if (t + 3 < t_hi) map_prefetch(hd.ks, k0 + 3 * BN, dma, mv[0]);
+      } else {
+        if (append_v) append_from_lds<VROW * 2>(hd.vs, vc_w, k0, sV[bk], stid);
+        if (t + 1 < t_hi) dma_tile<PAGED>(hd.vs, k0 + BN, sV[bn], dma, mv[0]);
+        if constexpr (PAGED)
+          if (t + 2 < t_hi) map_prefetch(hd.vs, k0 + 2 * BN, dma, mv[0]);
+      }
     }
 
     // step b: unit (t, keys 32..63)

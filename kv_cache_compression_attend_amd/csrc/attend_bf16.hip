@@ -77,10 +77,9 @@
 //     flag; waves 4-7 load K, waves 0-3 load V) in four LDS buffers per
 //     operand, in pairs: one barrier per two 64-key tiles publishes the next
 //     two tiles of K and V, the K waves load two tiles at that barrier and
-//     the V waves two at the start of the following tile.  With S-CAS, whose
-//     sums take the room of the fourth buffer, three buffers, a tile ahead,
-//     one barrier per tile.  V stays row-major and the value product reads
-//     its transposed fragments with the CDNA4 transposing LDS read.  Pooled
+//     the V waves two at the start of the following tile.  V stays
+//     row-major and the value product reads its transposed fragments with
+//     the CDNA4 transposing LDS read.  Pooled
 //     caches, whose rows are found through a map, read each burst's pool
 //     rows one burst ahead.  The first and last tiles are separate
 //     instantiations, so the steady-state step is straight-line code.  (The
@@ -570,12 +569,13 @@ __device__ __forceinline__ void write_split(const AttendArgs& a, const Head& hd,
 // accumulator of every source segment they fall in.  Source src < step
 // covers cache rows [lenb[src], lenb[src+1]); the current scale covers
 // [Lc, Ltot).  Bounds are wave-uniform scalar loads.
-template <int NT, typename Prob>
+template <typename Prob>
 __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, int hf,
-                                         const Prob& prob, float psum, int kblk, float* sc) {
+                                         const Prob& prob, float psum, int kblk,
+                                         float (&sc)[kMaxScales]) {
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
-    if (src > a.step) break;
+    if (src > a.step) continue;  // (not break: the loop must unroll fully, sc stays in registers)
     const int lo = hd.lenb[src];
     const int hi = src < a.step ? hd.lenb[src + 1] : hd.Ltot;
     if (lo < hi && lo < kblk + 32 && hi > kblk) {
@@ -589,22 +589,20 @@ __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, in
           acc += (key >= lo && key < hi) ? prob(v) : 0.f;
         }
       }
-      sc[src * NT] += acc;
+      sc[src] += acc;
     }
   }
 }
 
-// Per-lane S-CAS accumulators: sc[src * NT] (NT: the workgroup's threads) is this query's
-// unnormalised mass on source src, relative to the running max.  Most 32-key
-// blocks lie inside one source segment, so their mass goes to one open
-// accumulator in a register (acc, for source cur, whose keys end at hi); only
-// a block that crosses a segment boundary walks the segment list (scas_add)
-// and moves the open segment on, at most once per source per workgroup.  The
-// per-source sums are touched only there, on a rescale and at the end, so
-// they live in LDS (the lane's own column of a [kMaxScales][threads] array):
-// 16 registers fewer for the loop.
+// Per-lane S-CAS accumulators: sc[src] is this query's unnormalised mass on
+// source src, relative to the running max.  Most 32-key blocks lie inside
+// one source segment, so their mass goes to one open accumulator (acc, for
+// source cur, whose keys end at hi); only a block that crosses a segment
+// boundary walks the segment list (scas_add) and moves the open segment on,
+// at most once per source per workgroup.  The per-source sums are indexed
+// only by unrolled loops (cur is wave-uniform), so they stay in registers.
 struct ScasAcc {
-  float* sc;
+  float sc[kMaxScales];
   float acc;
   int cur, hi;
 };
@@ -621,40 +619,37 @@ __device__ __forceinline__ void scas_open(const AttendArgs& a, const Head& hd, S
   x.hi = seg_hi(a, hd, src);
 }
 
-template <int NT>
-__device__ __forceinline__ void scas_init(const AttendArgs& a, const Head& hd, ScasAcc& x,
-                                          float* lds) {
-  x.sc = lds + threadIdx.x;
+__device__ __forceinline__ void scas_init(const AttendArgs& a, const Head& hd, ScasAcc& x) {
 #pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) x.sc[s * NT] = 0.f;
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s] = 0.f;
   x.acc = 0.f;
   scas_open(a, hd, x, 0);
 }
 
-template <int NT>
 __device__ __forceinline__ void scas_flush(ScasAcc& x) {
-  x.sc[x.cur * NT] += x.acc;
+#pragma unroll
+  for (int s = 0; s < kMaxScales; ++s)
+    if (s == x.cur) x.sc[s] += x.acc;
   x.acc = 0.f;
 }
 
-template <int NT>
 __device__ __forceinline__ void scas_rescale(ScasAcc& x, float corr) {
 #pragma unroll
-  for (int s = 0; s < kMaxScales; ++s) x.sc[s * NT] *= corr;
+  for (int s = 0; s < kMaxScales; ++s) x.sc[s] *= corr;
   x.acc *= corr;
 }
 
 // Adds one 32-key block (keys kblk.., this lane's probabilities prob(v),
 // v = 0..15, summing to psum); blocks are added in key order.
-template <int NT, typename Prob>
+template <typename Prob>
 __device__ __forceinline__ void scas_block(const AttendArgs& a, const Head& hd, int hf,
                                            const Prob& prob, float psum, int kblk, ScasAcc& x) {
   if (kblk + 32 <= x.hi) {
     x.acc += psum;
     return;
   }
-  scas_flush<NT>(x);
-  scas_add<NT>(a, hd, hf, prob, psum, kblk, x.sc);
+  scas_flush(x);
+  scas_add(a, hd, hf, prob, psum, kblk, x.sc);
   scas_open(a, hd, x, kblk + 32);
 }
 
@@ -666,7 +661,7 @@ __device__ __forceinline__ void scas_reduce(const AttendArgs& a, const Head& hd,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
-    const float own = x.sc[src * WAVES * 64];
+    const float own = x.sc[src];
     float m = (own + __shfl_xor(own, 32)) * inv;
     m = qrow < hd.n ? m : 0.f;
 #pragma unroll
@@ -693,7 +688,6 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VSTR];
   __shared__ float sRed[SCAS ? 4 * kMaxScales : 1];
-  __shared__ float sScas[SCAS ? kMaxScales * 256 : 1];
 
   const Head hd = setup(a);
   const int tid = threadIdx.x;
@@ -710,7 +704,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   ScasAcc sa;
-  if constexpr (SCAS) scas_init<256>(a, hd, sa, sScas);
+  if constexpr (SCAS) scas_init(a, hd, sa);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -800,7 +794,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
         l_run *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db) oacc[db] *= corr;
-        if constexpr (SCAS) scas_rescale<256>(sa, corr);
+        if constexpr (SCAS) scas_rescale(sa, corr);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) ps[kb] = exp_pack<SCAS>(s[kb], c2, m_run, pb[kb]);
       }
@@ -808,7 +802,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
     l_run += ps[0] + ps[1];
     if constexpr (SCAS) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) scas_block<256>(a, hd, hf, ProbOf{s[kb], c2, m_run}, ps[kb], k0 + 32 * kb, sa);
+      for (int kb = 0; kb < 2; ++kb) scas_block(a, hd, hf, ProbOf{s[kb], c2, m_run}, ps[kb], k0 + 32 * kb, sa);
     }
 
 #pragma unroll
@@ -826,7 +820,7 @@ __global__ __launch_bounds__(256, SCAS ? 1 : 2) void attend_q128_kernel(AttendAr
   const float inv = 1.f / (l_run + __shfl_xor(l_run, 32));
   store_out(a, hd, qrow, hf, oacc, inv);
   if constexpr (SCAS) {
-    scas_flush<256>(sa);
+    scas_flush(sa);
     scas_reduce<4>(a, hd, qrow, inv, sa, sRed);
   }
 }
@@ -887,14 +881,13 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* ws_o, 
 // gives (tile loads take per-lane pool offsets).
 template <bool SCAS, bool SPLIT, bool PAGED, bool PRE>
 __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
-  // LDS buffers per operand, and how many tiles ahead of its first use the
-  // direct staging loads a tile (the S-CAS sums leave room for three).
-  constexpr int NBUF = SCAS ? 3 : 4;
+  // LDS buffers per operand: tiles in pairs (PD = 2, one barrier per two
+  // tiles) in four.
+  constexpr int NBUF = 4;
   constexpr int PD = NBUF - 2;
   __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][BN * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][BN * VROW];
   __shared__ float sRed[SCAS ? 8 * kMaxScales : 1];
-  __shared__ float sScas[SCAS ? kMaxScales * 512 : 1];
 
   const Head hd = setup(a);
   const int tid = threadIdx.x;
@@ -932,7 +925,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   for (int db = 0; db < 4; ++db) o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
   ScasAcc sa;
-  if constexpr (SCAS) scas_init<512>(a, hd, sa, sScas);
+  if constexpr (SCAS) scas_init(a, hd, sa);
 
   const int kb_row = permuted_row(j);
   const int Ltot = hd.Ltot;
@@ -1042,7 +1035,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
         l_run *= corr;
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] *= corr;
-        if constexpr (SCAS) scas_rescale<512>(sa, corr);
+        if constexpr (SCAS) scas_rescale(sa, corr);
         psum = exp_pack<SCAS>(s, c2, m_run, p);
       }
     }
@@ -1112,22 +1105,15 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
 #pragma unroll
   for (int half = 0; half < 2; ++half) p1[half].u = u32x4{0, 0, 0, 0};
 
-  // Prologue: K(t_lo) in buffer 0; with register staging K(t_lo + 1)
-  // (waves 4-7) and V(t_lo) (waves 0-3) in registers, with direct staging
-  // in their LDS buffers.  Every split holds at least one tile.
+  // Prologue: K(t_lo), K(t_lo + 1), K(t_lo + 2) (waves 4-7) and V(t_lo),
+  // V(t_lo + 1) (waves 0-3) in LDS buffers 0, 1, 2.  Every split holds at
+  // least one tile.
   char* const kc_w = const_cast<char*>(hd.ks.cache);
   char* const vc_w = const_cast<char*>(hd.vs.cache);
   const int k_lo = t_lo * BN;
-  // The first tile at or after the current one whose append falls to this
-  // workgroup; kept uniform (updated outside the stager branches) so that it
-  // stays in a scalar register.
-  int next_append = first_append_tile(a, hd, t_lo);
   // Whether this workgroup writes key tile x of the current scale into the
   // cache (fused append: tile x falls to the q-tile x mod n_qtiles).
   auto owns = [&](int x) { return hd.append && x % a.n_qtiles == hd.qt; };
-  // Direct staging: K(t_lo) and V(t_lo) straight into LDS, with K(t_lo + 1)
-  // (one-tile lead, S-CAS) or K(t_lo + 1), K(t_lo + 2) and V(t_lo + 1)
-  // (paired tiles: the loads of two tiles are published by one barrier).
   // Pooled caches read each tile's pool rows first (map_prefetch), the
   // prologue's tiles one after another and the first burst's ahead.
   if (kstager) {
@@ -1184,9 +1170,6 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     const int k0 = t * BN;
     const int bn = bk == NBUF - 1 ? 0 : bk + 1;
     const int bp = bk == 0 ? NBUF - 1 : bk - 1;
-    const bool append_v = hd.append && t == next_append;  // V(t)
-    if (t == next_append) next_append += a.n_qtiles;
-    const bool append_k = hd.append && t + 1 == next_append;  // K(t + 1)
     if constexpr (PD == 2) {
       // Paired tiles, odd tile t (no barrier): the V-staging waves load
       // V(t + 1) and V(t + 2) into the buffers of V(t - 3) and V(t - 2), both
@@ -1210,7 +1193,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
                     std::true_type{}, s0, p0, fast_c);
     if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
     else settle(s0, p0, e0);
-    if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
+    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
     if constexpr (PD == 2) {
       // Paired tiles, one barrier every second tile (t - t_lo even).  By the
       // barrier of tile t, K(t + 1), K(t + 2), V(t) and V(t + 1) have landed
@@ -1242,25 +1225,6 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
               append_from_lds<VROW * 2>(hd.vs, vc_w, k0 + x * BN, sV[(bk + x) % NBUF], stid);
         }
       }
-    } else {
-      // One tile ahead (S-CAS): K(t + 1) and V(t) have landed (each wave
-      // waits for its own loads; the barrier publishes them).  Then the
-      // appends, and the loads of K(t + 2) and V(t + 1) into the buffers that
-      // K(t - 1) and V(t - 2) leave (both last read in step a of the previous
-      // tile).
-      wait_loads();
-      barrier_keep_loads();
-      if (kstager) {
-        if (append_k && t + 1 < t_hi) append_from_lds<KSTR * 2>(hd.ks, kc_w, k0 + BN, sK[bn], stid);
-        if (t + 2 < t_hi) dma_tile<PAGED>(hd.ks, k0 + 2 * BN, sK[bp], dma, mv[0]);
-        if constexpr (PAGED)
-          if (t + 3 < t_hi) map_prefetch(hd.ks, k0 + 3 * BN, dma, mv[0]);
-      } else {
-        if (append_v) append_from_lds<VROW * 2>(hd.vs, vc_w, k0, sV[bk], stid);
-        if (t + 1 < t_hi) dma_tile<PAGED>(hd.vs, k0 + BN, sV[bn], dma, mv[0]);
-        if constexpr (PAGED)
-          if (t + 2 < t_hi) map_prefetch(hd.vs, k0 + 2 * BN, dma, mv[0]);
-      }
     }
 
     // step b: unit (t, keys 32..63)
@@ -1269,7 +1233,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
                     std::integral_constant<bool, !LAST>{}, s1, p1, fast_c);
     if constexpr (FAST) settle_fast(s1, p1, e1, s0, false);
     else settle(s1, p1, e1);
-    if constexpr (SCAS) scas_block<512>(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
+    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
     bk = bn;
   };
   using T_ = std::true_type;
@@ -1300,7 +1264,7 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   const float inv = 1.f / l_tot;
   store_out(a, hd, qrow, hf, o, inv);
   if constexpr (SCAS) {
-    scas_flush<512>(sa);
+    scas_flush(sa);
     scas_reduce<8>(a, hd, qrow, inv, sa, sRed);
   }
 }

@@ -450,6 +450,36 @@ def test_determinism_and_scas_repeat():
     ctx.close()
 
 
+def test_split_merge_is_deterministic():
+    """A split launch's partials are merged in split order, whatever order its
+    workgroups finish in: the largest split launch of the full-cache layer,
+    repeated, gives identical output bits."""
+    wl = workloads.get("c1")
+    keep = _schedule(wl)
+    ctx = hk.Context(1, 16, 128, 1, wl.scale_tokens, keep, torch.bfloat16)
+    split_steps = [t for t in range(wl.n_scales) if ctx.attend_plan(t)[1] > 1]
+    assert split_steps, "no split launch in this workload"
+    last = split_steps[-1]
+    for t in range(last):
+        inp = workloads.step_inputs(wl, 0, t)
+        k, v = to_device(inp.k, wl), to_device(inp.v, wl)
+        ctx.append_scale(0, 1, t, k, v)
+    inp = workloads.step_inputs(wl, 0, last)
+    q, k, v = to_device(inp.q, wl), to_device(inp.k, wl), to_device(inp.v, wl)
+    ref = None
+    for rep in range(12):
+        out = torch.full_like(q, float("nan"))
+        note(f"split merge rep {rep} step {last} splits {ctx.attend_plan(last)[1]}")
+        ctx.attend(0, last, q, k, v, out, 1.0)
+        got = out.view(torch.int16).cpu().numpy()
+        if ref is None:
+            ref = got
+            assert torch.isfinite(out).all()
+        else:
+            assert np.array_equal(ref, got), rep
+    ctx.close()
+
+
 def test_order_and_argument_errors():
     wl = _custom(50, "errors", (1, 2, 3), heads=2, head_dim=128, batch=1, dtype="bf16")
     keep = np.ones((1, 2, 3), dtype=np.uint8)

@@ -565,10 +565,19 @@ __device__ __forceinline__ void write_split(const AttendArgs& a, const Head& hd,
   if (hf == 0) a.ws_ml[row] = make_float2(m, l);
 }
 
+// The head's segment bounds for S-CAS: cache rows held before scale src.
+// The table is not written while a launch runs, so it is read through the
+// constant address space: the loads are scalar (their waits do not wait for
+// the tiles in flight, as vector loads' would) and land in scalar registers.
+typedef __attribute__((address_space(4))) const int32_t const_i32;
+__device__ __forceinline__ int seg_lo(const Head& hd, int src) {
+  return ((const const_i32*)hd.lenb)[src];
+}
+
 // Adds this lane's probabilities of keys [kblk, kblk + 32) to the
 // accumulator of every source segment they fall in.  Source src < step
 // covers cache rows [lenb[src], lenb[src+1]); the current scale covers
-// [Lc, Ltot).  Bounds are wave-uniform scalar loads.
+// [Lc, Ltot).
 template <typename Prob>
 __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, int hf,
                                          const Prob& prob, float psum, int kblk,
@@ -576,8 +585,8 @@ __device__ __forceinline__ void scas_add(const AttendArgs& a, const Head& hd, in
 #pragma unroll
   for (int src = 0; src < kMaxScales; ++src) {
     if (src > a.step) continue;  // (not break: the loop must unroll fully, sc stays in registers)
-    const int lo = hd.lenb[src];
-    const int hi = src < a.step ? hd.lenb[src + 1] : hd.Ltot;
+    const int lo = seg_lo(hd, src);
+    const int hi = src < a.step ? seg_lo(hd, src + 1) : hd.Ltot;
     if (lo < hi && lo < kblk + 32 && hi > kblk) {
       float acc = 0.f;
       if (lo <= kblk && hi >= kblk + 32) {
@@ -608,7 +617,7 @@ struct ScasAcc {
 };
 
 __device__ __forceinline__ int seg_hi(const AttendArgs& a, const Head& hd, int src) {
-  return src < a.step ? hd.lenb[src + 1] : hd.Ltot;
+  return src < a.step ? seg_lo(hd, src + 1) : hd.Ltot;
 }
 
 // The open segment: the first source whose keys end after key k.

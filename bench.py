@@ -379,6 +379,28 @@ def main():
         print(json.dumps({"copy_probe_bytes_each": src.numel() * 2, "copies": 3}), flush=True)
         return
 
+    # ---------------- main workload: one full-cache Infinity-2B-shaped layer ----------------
+    # Its inputs are drawn on the host before the other workloads run, so
+    # that no host-side work idles the GPU between their passes (which bring
+    # it to its sustained clock) and the main line's timed passes.
+    if not args.sections_only:
+        wl = workloads.get("c1")
+        table = workloads.dirichlet_scas(wl)
+        keep, _, _ = hk.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
+        ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
+                         torch.bfloat16)
+        K, L = wl.n_scales, wl.layers
+        qs, kall, vall, outs = [], [], [], []
+        for t in range(K):
+            ins = [workloads.step_inputs(wl, l, t) for l in range(L)]
+            to = lambda a: torch.from_numpy(np.stack(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa
+            qs.append(to([x.q for x in ins]))
+            kall.append(to([x.k for x in ins]))
+            vall.append(to([x.v for x in ins]))
+            outs.append(torch.empty_like(qs[-1][0]))
+        flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
+        total_flops = sum(flops.values())
+
     # ---------------- the other workloads ----------------
     # They run first: the GPU then reaches its sustained clock (it needs ~100
     # ms of work after the host-side set-up) before the main line's timed
@@ -417,23 +439,6 @@ def main():
         print(json.dumps(result), flush=True)
         return
 
-    # ---------------- main workload: one full-cache Infinity-2B-shaped layer ----------------
-    wl = workloads.get("c1")
-    table = workloads.dirichlet_scas(wl)
-    keep, _, _ = hk.build_schedule(table, wl.scale_tokens, wl.budget, wl.n_sink)
-    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, keep,
-                     torch.bfloat16)
-    K, L = wl.n_scales, wl.layers
-    qs, kall, vall, outs = [], [], [], []
-    for t in range(K):
-        ins = [workloads.step_inputs(wl, l, t) for l in range(L)]
-        to = lambda a: torch.from_numpy(np.stack(a).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa
-        qs.append(to([x.q for x in ins]))
-        kall.append(to([x.k for x in ins]))
-        vall.append(to([x.v for x in ins]))
-        outs.append(torch.empty_like(qs[-1][0]))
-    flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
-    total_flops = sum(flops.values())
     if args.data_sensitivity:
         print(json.dumps(data_sensitivity(ctx, wl, qs, kall, vall, outs, stream, torch)), flush=True)
         return

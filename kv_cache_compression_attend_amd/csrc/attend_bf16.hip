@@ -1166,8 +1166,13 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   wait_loads();
   barrier_keep_loads();
   if (kstager && owns(t_lo)) append_from_lds<KSTR * 2>(hd.ks, kc_w, k_lo, sK[0], stid);
-  qk(sK[0], 0, s0);
-  if constexpr (PRE) {
+  // A wave whose 32 queries all lie past the scale's end (the last query tile
+  // of a scale that does not fill it) computes nothing: it only stages its
+  // share of the tiles and meets the barriers, so its SIMD's other wave has
+  // the matrix pipe to itself.
+  const bool idle = __builtin_amdgcn_readfirstlane(hd.qt * 256 + wave * 32) >= hd.n;
+  if (!idle) qk(sK[0], 0, s0);
+  if (PRE && !idle) {
     // The first unit (it always holds a valid key) sets the reference: 0
     // when its exact max lies within +-kFastRange for every query of the
     // wave (the first tile's probabilities are then already those of fast
@@ -1185,10 +1190,11 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
   // absent next tile and enables the tail mask, which only the head's final
   // tile needs.
   int bk = 0;  // LDS buffer of K(t) and of V(t)
-  auto tile = [&](int t, auto first_c, auto last_c, auto fast_c) {
+  auto tile = [&](int t, auto first_c, auto last_c, auto fast_c, auto idle_c) {
     constexpr bool FIRST = decltype(first_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     constexpr bool FAST = decltype(fast_c)::value;
+    constexpr bool IDLE = decltype(idle_c)::value;
     const int k0 = t * BN;
     const int bn = bk == NBUF - 1 ? 0 : bk + 1;
     const int bp = bk == 0 ? NBUF - 1 : bk - 1;
@@ -1210,12 +1216,14 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
       }
     }
     // step a: unit (t, keys 0..31)
-    if constexpr (LAST) mask_tail(s0, k0);
-    float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
-                    std::true_type{}, s0, p0, fast_c);
-    if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
-    else settle(s0, p0, e0);
-    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
+    if constexpr (!IDLE) {
+      if constexpr (LAST) mask_tail(s0, k0);
+      float e0 = step(sV[bp], 1, p1, std::integral_constant<bool, !FIRST>{}, sK[bk], 1, s1,
+                      std::true_type{}, s0, p0, fast_c);
+      if constexpr (FAST) settle_fast(s0, p0, e0, s1, true);
+      else settle(s0, p0, e0);
+      if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s0, c2, m_run}, e0, k0, sa);
+    }
     if constexpr (PD == 2) {
       // Paired tiles, one barrier every second tile (t - t_lo even).  By the
       // barrier of tile t, K(t + 1), K(t + 2), V(t) and V(t + 1) have landed
@@ -1250,32 +1258,37 @@ __global__ __launch_bounds__(512) void attend_q256_kernel(AttendArgs a) {
     }
 
     // step b: unit (t, keys 32..63)
-    if constexpr (LAST) mask_tail(s1, k0 + 32);
-    float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
-                    std::integral_constant<bool, !LAST>{}, s1, p1, fast_c);
-    if constexpr (FAST) settle_fast(s1, p1, e1, s0, false);
-    else settle(s1, p1, e1);
-    if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
+    if constexpr (!IDLE) {
+      if constexpr (LAST) mask_tail(s1, k0 + 32);
+      float e1 = step(sV[bk], 0, p0, std::true_type{}, sK[bn], 0, s0,
+                      std::integral_constant<bool, !LAST>{}, s1, p1, fast_c);
+      if constexpr (FAST) settle_fast(s1, p1, e1, s0, false);
+      else settle(s1, p1, e1);
+      if constexpr (SCAS) scas_block(a, hd, hf, ProbOf{s1, c2, m_run}, e1, k0 + 32, sa);
+    }
     bk = bn;
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  if (t_hi - t_lo == 1) {
-    tile(t_lo, T_{}, T_{}, F_{});
+  if (idle) {
+    // The same tiles, so the same loads, appends and barriers.
+    for (int t = t_lo; t < t_hi; ++t) tile(t, F_{}, F_{}, F_{}, T_{});
+  } else if (t_hi - t_lo == 1) {
+    tile(t_lo, T_{}, T_{}, F_{}, F_{});
   } else {
-    tile(t_lo, T_{}, F_{}, F_{});
+    tile(t_lo, T_{}, F_{}, F_{}, F_{});
     int t = t_lo + 1;
     if constexpr (PRE) {
       // Where the reference is still 0 after the first tile for every query
       // of the wave, the middle tiles run in fast mode until a block leaves
       // the range.
       fast = __all(m_run == 0.f);
-      for (; fast && t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, T_{});
+      for (; fast && t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, T_{}, F_{});
     }
-    for (; t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, F_{});
-    tile(t_hi - 1, F_{}, T_{}, F_{});
+    for (; t + 1 < t_hi; ++t) tile(t, F_{}, F_{}, F_{}, F_{});
+    tile(t_hi - 1, F_{}, T_{}, F_{}, F_{});
   }
-  pv(sV[bk == 0 ? NBUF - 1 : bk - 1], 1, p1);
+  if (!idle) pv(sV[bk == 0 ? NBUF - 1 : bk - 1], 1, p1);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if constexpr (SPLIT) {

@@ -775,6 +775,7 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
     static_flops = pass_flops(wl, keep, lenb_table(keep, wl.scale_tokens))
     ms, cache_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3)
     ms_pool, pool_bytes = expiry_pass(args, hk, wl, expire, torch, dev, stream, 3, pooled=True)
+    appends = progressive_appends(args, hk, wl, expire, torch, np, dev, stream)
     row_bytes = wl.head_dim * 2
     gather_bytes = sum(moved_rows(expire, wl.scale_tokens, t) for t in range(K)) * wl.batch \
         * row_bytes * 2 * 2
@@ -798,10 +799,67 @@ def progressive_rate(args, hk, workloads, torch, np, dev, stream):
             "per_head_regions": {"allocated_cache_GB": round(cache_bytes / 1e9, 3),
                                  "ms_per_pass": round(ms, 3),
                                  "note": "each head sized to its own peak; dropped segments "
-                                         "removed by an in-place gather"},
+                                         "removed by an in-place gather",
+                                 "appends": appends},
             "static_allocated_cache_GB": round(hk.layout(wl.scale_tokens, keep, wl.batch,
                                                          wl.head_dim)[0] * 2 * 2 / 1e9, 3),
             "passes": args.pruned_steps}
+
+
+def progressive_appends(args, hk, wl, expire, torch, np, dev, stream):
+    """The appends of the progressive schedule on per-head regions, one
+    all-layer hk_append_scale per completed scale, issued once every layer has
+    attended the scale (the order the gather needs): the in-place gather of
+    the segments that leave, then the compaction of the new scale.  GB/s of
+    read + write bytes from events around each append."""
+    K, L = wl.n_scales, wl.layers
+    ctx = hk.Context(wl.layers, wl.heads, wl.head_dim, wl.batch, wl.scale_tokens, None,
+                     torch.bfloat16, expire=expire)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    qs, kall, vall, outs = [], [], [], []
+    for t in range(K - 1):
+        shape = (L, wl.batch, wl.scale_tokens[t], wl.heads, wl.head_dim)
+        qs.append((torch.randn(shape[1:], generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        kall.append((torch.randn(shape, generator=g, device=dev) * wl.qk_std).to(torch.bfloat16))
+        vall.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
+        outs.append(torch.empty_like(qs[-1]))
+    row_bytes = wl.head_dim * 2
+    nbytes, gbytes = {}, {}
+    for t in range(K - 1):
+        stored = int((expire[:, :, t] > t).sum())
+        gbytes[t] = moved_rows(expire, wl.scale_tokens, t) * wl.batch * row_bytes * 2 * 2
+        nbytes[t] = gbytes[t] + stored * wl.batch * wl.scale_tokens[t] * row_bytes * 2 * 2
+    ev = {t: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for t in range(K - 1)}
+    times = {t: [] for t in range(K - 1)}
+    for rep in range(4):
+        ctx.reset()
+        gpu_sleep(torch)
+        for t in range(K - 1):
+            for l in range(L):
+                ctx.attend(l, t, qs[t], kall[t][l], vall[t][l], outs[t], wl.softmax_scale,
+                           stream=stream)
+            ev[t][0].record(stream)
+            ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+            ev[t][1].record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            for t in range(K - 1):
+                times[t].append(ev[t][0].elapsed_time(ev[t][1]))
+    ctx.close()
+    ms = {t: float(np.mean(times[t])) for t in times}
+    moving = [t for t in ms if gbytes[t] > 0]
+    total = sum(nbytes.values())
+    gbps = total / (sum(ms.values()) * 1e-3) / 1e9
+    return {"what": "one all-layer append per completed scale (in-place gather, then compaction), "
+                    "events around each append",
+            "bytes_per_pass": float(total), "gather_bytes_per_pass": float(sum(gbytes.values())),
+            "ms_per_pass": round(sum(ms.values()), 4),
+            "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+            "steps_with_moves_GBps": round(sum(nbytes[t] for t in moving) /
+                                           (sum(ms[t] for t in moving) * 1e-3) / 1e9, 1),
+            "per_step_GBps": {t: round(nbytes[t] / (ms[t] * 1e-3) / 1e9, 1) for t in ms}}
 
 
 def expiry_pass(args, hk, wl, expire, torch, dev, stream, seed, keep=None, sub_blocks=None,
@@ -999,6 +1057,21 @@ def compact_rate(args, hk, workloads, torch, np, dev, stream):
         if rep:
             for t in range(K - 1):
                 times[t].append(ev[t][0].elapsed_time(ev[t][1]))
+    # The whole pass: one event pair around the 12 appends (the per-step
+    # events above each add a few microseconds between launches).
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    whole = []
+    for rep in range(4):
+        ctx.reset()
+        gpu_sleep(torch)
+        e0.record(stream)
+        for t in range(K - 1):
+            ctx.append_scale(0, L, t, kall[t], vall[t], stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if rep:
+            whole.append(e0.elapsed_time(e1))
+    whole_gbps = sum(nbytes.values()) / (float(np.mean(whole)) * 1e-3) / 1e9
     ms = {t: float(np.mean(times[t])) for t in times}
     big = max(nbytes, key=lambda t: nbytes[t])
     total = sum(nbytes.values()) / (sum(ms.values()) * 1e-3) / 1e9
@@ -1006,6 +1079,10 @@ def compact_rate(args, hk, workloads, torch, np, dev, stream):
     ctx.close()
     return {"workload": "infinity2b-l32-b4 full cache: one all-layer append per completed scale",
             "bound": "hbm", "GBps": round(total, 1), "frac_hbm": round(total / PEAK_HBM_GBPS, 4),
+            "timing": "GBps: bytes of the pass over the sum of per-append event times; "
+                      "whole_pass: one event pair around the pass's appends",
+            "whole_pass_GBps": round(whole_gbps, 1),
+            "whole_pass_frac_hbm": round(whole_gbps / PEAK_HBM_GBPS, 4),
             "largest_step": big, "largest_step_bytes": nbytes[big],
             "largest_step_GBps": round(bigr, 1), "largest_step_frac_hbm": round(bigr / PEAK_HBM_GBPS, 4),
             "per_step_GBps": {t: round(nbytes[t] / (ms[t] * 1e-3) / 1e9, 1) for t in ms}}

@@ -74,11 +74,15 @@ __global__ __launch_bounds__(kCopyThreads) void compact_kernel(CompactArgs a) {
 // of arXiv 2605.14877, Figure 4 caption: a pruning set that grows is to be gone
 // from the cache once its scale is done, so segments leave from the middle of the cache).
 //
-// Destination rows are rewritten in ascending chunks, one workgroup per
-// region.  Every destination row's source row lies at or above it, so within
-// a chunk all loads finish (barrier) before any store, and the loads of later
-// chunks start above every row stored so far: no byte is read after this
-// launch has written it, and no source byte is overwritten before it is read.
+// Destination rows are rewritten in ascending chunks by one workgroup per
+// (region, column part).  Every destination row's source row lies at or above
+// it, so within a chunk all loads finish (barrier) before any store, and the
+// loads of later chunks start above every row stored so far: no byte is read
+// after this launch has written it, and no source byte is overwritten before
+// it is read.  A region's rows are split by columns into a.parts parts of
+// whole 128-byte lines (blockIdx.z): the parts touch disjoint bytes, so each
+// is an independent move of its own, and a region's chain of chunks is
+// a.parts times shorter than with one workgroup per region.
 __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
   __shared__ GatherRun runs[kMaxScales];
   const GatherDesc d = a.desc[blockIdx.x];
@@ -88,22 +92,23 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
   const int64_t region = d.base + int64_t(blockIdx.y) * d.cap * a.row_bytes;
   uint8_t* kc = a.kcache + region;
   uint8_t* vc = a.vcache + region;
-  const int cpr = a.row_bytes >> 4;
+  const int cmask = (1 << a.cpp_shift) - 1;              // vectors per part - 1
+  const int col0 = int(blockIdx.z) << a.cpp_shift;       // first vector of this part
   for (int row0 = d.dst_begin; row0 < d.dst_end; row0 += a.rows_per_chunk) {
-    const int items = min(a.rows_per_chunk, d.dst_end - row0) * cpr;
+    const int items = min(a.rows_per_chunk, d.dst_end - row0) << a.cpp_shift;
     u32x4 kv[kGatherItems], vv[kGatherItems];
 #pragma unroll
     for (int u = 0; u < kGatherItems; ++u) {
       const int it = threadIdx.x + u * kCopyThreads;
       if (it < items) {
-        const int row = row0 + it / cpr;
+        const int row = row0 + (it >> a.cpp_shift);
         int src = row;
         for (int r = 0; r < d.n_runs; ++r)
           if (row < runs[r].dst + runs[r].rows) {
             src = runs[r].src + (row - runs[r].dst);
             break;
           }
-        const int64_t off = int64_t(src) * a.row_bytes + (it % cpr) * 16;
+        const int64_t off = int64_t(src) * a.row_bytes + (col0 + (it & cmask)) * 16;
         kv[u] = *reinterpret_cast<const u32x4*>(kc + off);
         vv[u] = *reinterpret_cast<const u32x4*>(vc + off);
       }
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
     for (int u = 0; u < kGatherItems; ++u) {
       const int it = threadIdx.x + u * kCopyThreads;
       if (it < items) {
-        const int64_t off = int64_t(row0) * a.row_bytes + int64_t(it) * 16;
+        const int64_t off = int64_t(row0 + (it >> a.cpp_shift)) * a.row_bytes + (col0 + (it & cmask)) * 16;
         __builtin_nontemporal_store(kv[u], reinterpret_cast<u32x4*>(kc + off));
         __builtin_nontemporal_store(vv[u], reinterpret_cast<u32x4*>(vc + off));
       }
@@ -123,9 +128,12 @@ __global__ __launch_bounds__(kCopyThreads) void gather_kernel(GatherArgs a) {
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
   if (a.n_desc == 0) return hipSuccess;
-  if (!grid_fits(a.n_desc, kCopyThreads, a.B)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(gather_kernel, dim3(unsigned(a.n_desc), unsigned(a.B)), dim3(kCopyThreads), 0,
-                     s, a);
+  if (a.parts < 1 || (a.parts << a.cpp_shift) * 16 != a.row_bytes ||
+      (a.rows_per_chunk << a.cpp_shift) != kCopyThreads * kGatherItems)
+    return hipErrorInvalidValue;
+  if (!grid_fits(a.n_desc, kCopyThreads, a.B, a.parts)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(gather_kernel, dim3(unsigned(a.n_desc), unsigned(a.B), unsigned(a.parts)),
+                     dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -842,7 +842,12 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n_desc = int(glast - gfirst);
     a.B = c->B;
     a.row_bytes = c->D * c->elem_bytes;
-    a.rows_per_chunk = hk::kGatherChunkBytes / a.row_bytes;
+    // Column parts of whole 128-byte lines (rows of 128 bytes or less: one
+    // part); both sizes are powers of two here.
+    a.parts = std::max(1, a.row_bytes / hk::kGatherPartBytes);
+    a.cpp_shift = 0;
+    while ((a.parts * 16 << a.cpp_shift) < a.row_bytes) ++a.cpp_shift;
+    a.rows_per_chunk = (hk::kGatherChunkBytes / 16) >> a.cpp_shift;
     hipError_t e = hk::launch_gather(a, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "gather launch");
   }

@@ -16,7 +16,8 @@ namespace hk {
 // the fastest plain contiguous copy and the faster compaction of launches
 // with few head runs; 8 per lane the faster one when a launch has at least
 // kCopyLargeMinBlocks blocks of the large size.  The in-place gather walks its
-// region in kGatherChunkBytes chunks, one pass each.  Scales that most heads
+// region in chunks of kGatherChunkBytes per column part, one pass each; a
+// part is at most kGatherPartBytes of every row.  Scales that most heads
 // store are copied in token blocks (contiguous reads across all heads) when a
 // layer has at most kRowsMaxHeads heads (their destinations sit in LDS).
 constexpr int kCopyThreads = 256;
@@ -24,6 +25,7 @@ constexpr int kCopyBlockBytes = 16384;
 constexpr int kCopyBlockBytesLarge = 32768;
 constexpr int64_t kCopyLargeMinBlocks = 16384;
 constexpr int kGatherChunkBytes = 32768;
+constexpr int kGatherPartBytes = 128;
 constexpr int kRowsMaxHeads = 1024;
 
 // One kept (layer, head) segment of a completed scale, to be copied into the cache.
@@ -116,7 +118,9 @@ struct GatherArgs {
   uint8_t* vcache;
   int n_desc, B;
   int row_bytes;          // D * element size, a multiple of 16
-  int rows_per_chunk;     // rows moved per barrier interval
+  int parts;              // column parts per region: row_bytes = parts * 16 << cpp_shift
+  int cpp_shift;          // log2 of the 16-byte vectors per row in one part
+  int rows_per_chunk;     // rows moved per barrier interval: kCopyThreads * kGatherItems >> cpp_shift
 };
 
 // 4-bit storage (head_dim 128): a row of 128 channels is 64 bytes of codes

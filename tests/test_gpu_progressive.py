@@ -163,9 +163,9 @@ def _drive(wl, exp, mode, layers=None, scas=False, check_every_step=True, seed=0
 def test_handmade_expiry_moves_overlapping_chunks(mode):
     """Small drops under long survivors: moves of 116 to 273 rows shifted by
     1 to 16 rows, so source and destination overlap inside and across the
-    128-row chunks.  At step 5 the only change is a dropped tail segment
-    (head 2): nothing moves, but the new segment goes where the dropped one
-    was."""
+    gather's 256-row chunks of each 128-byte column part.  At step 5 the
+    only change is a dropped tail segment (head 2): nothing moves, but the
+    new segment goes where the dropped one was."""
     wl = _wl(90, (1, 2, 3, 4, 6, 8, 12, 16, 20), layers=1, heads=4, head_dim=128, batch=2,
              dtype="bf16")
     K = wl.n_scales

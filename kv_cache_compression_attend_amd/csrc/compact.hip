@@ -4,15 +4,15 @@
 // never written).
 //
 // A pure copy, bound by HBM bandwidth.  Two grids: token blocks (a scale
-// that most heads store: a workgroup reads a contiguous run of whole tokens,
+// that most heads store: a workgroup reads two consecutive whole tokens,
 // every head's 256-byte row of each, and writes each head's rows to that
 // head's run) and per head (one block of rows of one (segment, batch entry);
-// reads stride over the tokens).  Every lane moves 16-byte vectors and keeps
-// four (16 KB blocks) or, for per-head launches with many head runs, eight
-// (32 KB blocks) loads per tensor in flight before storing, one pass per
-// workgroup.  Loads and stores are nontemporal: the source is read once and
-// the next reader of the cache is a later attend launch.  Measured on the
-// MI355X with 1 GiB of K and of V: a contiguous copy with this structure
+// reads stride over the tokens).  Every lane moves 16-byte vectors; per-head
+// workgroups keep four (16 KB blocks) or, for launches with many head runs,
+// eight (32 KB blocks) loads per tensor in flight before storing, one pass
+// per workgroup.  Loads and stores are nontemporal: the source is read once
+// and the next reader of the cache is a later attend launch.  Measured on
+// the MI355X with 1 GiB of K and of V: a contiguous copy with this structure
 // moves 6.1 TB/s (5.75 with ordinary loads), the token-block pattern 5.96,
 // the per-head pattern (256 bytes per 4 KB token row) 5.30.
 #include "device.h"

@@ -19,7 +19,8 @@ namespace hk {
 // region in chunks of kGatherChunkBytes per column part, one pass each; a
 // part is at most kGatherPartBytes of every row.  Scales that most heads
 // store are copied in token blocks (contiguous reads across all heads) when a
-// layer has at most kRowsMaxHeads heads (their destinations sit in LDS).
+// layer has at most kRowsMaxHeads heads (their destinations sit in LDS), at
+// most kRowsTokens tokens per workgroup.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlockBytes = 16384;
 constexpr int kCopyBlockBytesLarge = 32768;
@@ -27,6 +28,7 @@ constexpr int64_t kCopyLargeMinBlocks = 16384;
 constexpr int kGatherChunkBytes = 32768;
 constexpr int kGatherPartBytes = 128;
 constexpr int kRowsMaxHeads = 1024;
+constexpr int kRowsTokens = 2;
 
 // One kept (layer, head) segment of a completed scale, to be copied into the cache.
 struct CopyDesc {

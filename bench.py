@@ -414,26 +414,27 @@ def main():
         raise SystemExit(f"unknown sections {sorted(unknown)}")
     if args.no_pruned or args.data_sensitivity:
         want = set()
-    # 32 layers, batch 8, 10% budget: scales/s per image
-    if "pruned" in want:
-        result["pruned_10pct"] = pruned_rate(args, hk, workloads, torch, np, dev, stream)
-    if "progressive" in want:
-        result["progressive_10pct"] = progressive_rate(args, hk, workloads, torch, np, dev, stream)
-    if "window" in want:
-        result["scale_window"] = window_rate(args, hk, workloads, torch, np, dev, stream)
-    if "int4" in want:
-        result["int4_10pct"] = int4_rate(args, hk, workloads, torch, np, dev, stream)
-    if "compact" in want:
-        result["compact"] = compact_rate(args, hk, workloads, torch, np, dev, stream)
-    if "infinity8b_4pct" in want:
-        result["infinity8b_4pct"] = infinity8b_rate(args, hk, workloads, torch, np, dev, stream,
-                                                    full_cache=False)
-    if "infinity8b_full_cache" in want:
-        result["infinity8b_full_cache"] = infinity8b_rate(args, hk, workloads, torch, np, dev,
-                                                          stream, full_cache=True)
-    # calibration: S-CAS cost and ranking stability
-    if "calibration" in want:
-        result["calibration"] = calibration_rate(args, hk, workloads, torch, np, dev, stream)
+    # Each section runs in turn; a line on stderr reports each one as it ends.
+    runners = [
+        ("pruned", "pruned_10pct", lambda: pruned_rate(args, hk, workloads, torch, np, dev, stream)),
+        ("progressive", "progressive_10pct",
+         lambda: progressive_rate(args, hk, workloads, torch, np, dev, stream)),
+        ("window", "scale_window", lambda: window_rate(args, hk, workloads, torch, np, dev, stream)),
+        ("int4", "int4_10pct", lambda: int4_rate(args, hk, workloads, torch, np, dev, stream)),
+        ("compact", "compact", lambda: compact_rate(args, hk, workloads, torch, np, dev, stream)),
+        ("infinity8b_4pct", "infinity8b_4pct",
+         lambda: infinity8b_rate(args, hk, workloads, torch, np, dev, stream, full_cache=False)),
+        ("infinity8b_full_cache", "infinity8b_full_cache",
+         lambda: infinity8b_rate(args, hk, workloads, torch, np, dev, stream, full_cache=True)),
+        ("calibration", "calibration",
+         lambda: calibration_rate(args, hk, workloads, torch, np, dev, stream)),
+    ]
+    for name, key, run in runners:
+        if name in want:
+            t0 = time.time()
+            result[key] = run()
+            print(f"[bench] section {name} done in {time.time() - t0:.1f} s", file=sys.stderr,
+                  flush=True)
 
     if args.sections_only:
         print(json.dumps(result), flush=True)
@@ -571,9 +572,12 @@ def main():
     torch.cuda.empty_cache()
     result.update(sections_out)
 
+    print(f"[bench] main line done: {result['value']} TFLOP/s", file=sys.stderr, flush=True)
+
     # ---------------- fp64 CPU oracle on a bounded sample ----------------
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args, wl, keep)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
     print(json.dumps(result), flush=True)
 
 

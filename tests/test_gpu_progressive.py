@@ -196,8 +196,10 @@ def test_progressive_bf16(mode):
     ctx.close()
 
 
-@pytest.mark.parametrize("head_dim", [16, 64])
+@pytest.mark.parametrize("head_dim", [16, 32, 64, 128])
 def test_progressive_f32(head_dim):
+    """fp32 rows of 64 to 512 bytes: the gather moves them as one column part
+    (head_dim 16 and 32), two (64) or four 128-byte parts (128)."""
     wl = _wl(92 + head_dim, (1, 2, 3, 4, 6, 8), layers=2, heads=3, head_dim=head_dim, batch=2,
              dtype="f32")
     exp = _schedule(wl, 0.35, 1, seed=9)

@@ -983,16 +983,20 @@ def calibration_rate(args, hk, workloads, torch, np, dev, stream):
             vs.append(torch.randn(shape, generator=g, device=dev).to(torch.bfloat16))
         return qs, ks, vs
 
-    def run(data, table):
+    def run(data, table, rec=None):
         qs, ks, vs = data
         ctx.reset()
         for t in range(K):
             for l in range(L):
+                if rec is not None and t == K - 1:
+                    rec[l][0].record(stream)
                 if table is None:
                     ctx.attend(l, t, qs[t][l], ks[t][l], vs[t][l], outs[t], 1.0, stream=stream)
                 else:
                     ctx.attend_with_scas_sum(l, t, qs[t][l], ks[t][l], vs[t][l], outs[t], 1.0, table,
                                              stream=stream)
+                if rec is not None and t == K - 1:
+                    rec[l][1].record(stream)
             if t < K - 1:
                 ctx.append_scale(0, L, t, ks[t], vs[t], stream=stream)
 
@@ -1012,6 +1016,21 @@ def calibration_rate(args, hk, workloads, torch, np, dev, stream):
     scratch = torch.zeros((L, wl.heads, K, K), dtype=torch.float64, device=dev)
     ms_plain = timed(lambda: run(data, None), 2)
     ms_scas = timed(lambda: run(data, scratch), 2)
+    # The final-scale attention launches of the plain pass (batch 4, 4,096
+    # queries x 10,521 keys per head), each timed with events on the launch
+    # stream, the pass queued behind a spin kernel; median over 3 passes.
+    final = []
+    for _ in range(3):
+        rec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(L)]
+        gpu_sleep(torch)
+        run(data, None, rec)
+        torch.cuda.synchronize()
+        final += [r[0].elapsed_time(r[1]) for r in rec]
+    final_flops = 4.0 * wl.head_dim * wl.scale_tokens[-1] * sum(wl.scale_tokens) * wl.heads * wl.batch
+    final_us = float(np.median(final)) * 1e3
+    final_tflops = final_flops / (final_us * 1e-6) / 1e12
+    final_plan = list(ctx.attend_plan(K - 1))
     tables = []
     for seed in (21, 22):
         tab = torch.zeros((L, wl.heads, K, K), dtype=torch.float64, device=dev)
@@ -1023,6 +1042,13 @@ def calibration_rate(args, hk, workloads, torch, np, dev, stream):
     return {"workload": "infinity2b-l32-b4-calibration: 32 layers x 16 heads, batch 4, full cache",
             "ms_per_pass_attend": round(ms_plain, 3), "ms_per_pass_with_scas": round(ms_scas, 3),
             "scas_overhead_ratio": round(ms_scas / ms_plain, 3),
+            "final_scale_attend": {"what": "final-scale attend launch without S-CAS (batch 4), median "
+                                           "of per-launch events over 3 passes x 32 layers",
+                                   "plan": final_plan,
+                                   "median_us": round(final_us, 2),
+                                   "flops_per_launch": final_flops,
+                                   "achieved_tflops": round(final_tflops, 2),
+                                   "frac": round(final_tflops / PEAK_BF16_TFLOPS, 4)},
             "ranking_stability": {"subsets": "two batches of 4 images (different draws)",
                                   "spearman_rho_per_source_scale": {s: round(float(r), 4) for s, r in enumerate(rho)
                                                                     if not np.isnan(r)},

@@ -173,6 +173,25 @@ def test_bf16_ragged_wide_launch(seed):
     run.ctx.close()
 
 
+@pytest.mark.parametrize("heads", [28, 48, 100])
+def test_token_block_compaction_head_counts(heads):
+    """All-layer appends of scales that most heads store go through the token
+    blocks: two tokens per workgroup at 28 heads (896 vectors, a partial
+    fourth slot per lane), one token at 48 (768) and at 100 (1,600 vectors,
+    two passes per workgroup).  One head drops a scale, so the blocks also
+    skip a head.  Cache bit for bit, outputs against the oracle."""
+    wl = _custom(100 + heads, f"token-blocks-h{heads}", (1, 3, 5, 8, 11), heads=heads, head_dim=128,
+                 batch=2, dtype="bf16", layers=2)
+    keep = np.ones((wl.layers, wl.heads, wl.n_scales), dtype=np.uint8)
+    keep[:, :, -1] = 0
+    keep[:, 1, 2] = 0
+    run = generate(wl, keep, [0, 1], multi_layer_append=True)
+    pairs = [(b, h) for b in range(wl.batch) for h in (0, 1, heads // 2, heads - 1)]
+    _compare_outputs(run, [0, 1], rows_per_unit=32, bh=pairs)
+    check_cache(run, [0, 1])
+    run.ctx.close()
+
+
 @pytest.mark.parametrize("case", ["full-b1", "pruned-b8", "ragged-f32", "ragged-bf16-scas", "wide-scas"])
 def test_fused_attend_append(case):
     """attend_append (attention and this scale's append in one call) leaves the

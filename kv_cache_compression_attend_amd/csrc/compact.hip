@@ -4,9 +4,9 @@
 // never written).
 //
 // A pure copy, bound by HBM bandwidth.  Two grids: token blocks (a scale
-// that most heads store: a workgroup reads two consecutive whole tokens,
-// every head's 256-byte row of each, and writes each head's rows to that
-// head's run) and per head (one block of rows of one (segment, batch entry);
+// that most heads store: a workgroup reads a few consecutive whole tokens
+// (8-16 KB per tensor), every head's row of each, and writes each head's
+// rows to that head's run) and per head (one block of rows of one (segment, batch entry);
 // reads stride over the tokens).  Every lane moves 16-byte vectors; per-head
 // workgroups keep four (16 KB blocks) or, for launches with many head runs,
 // eight (32 KB blocks) loads per tensor in flight before storing, one pass

@@ -872,12 +872,15 @@ int append_launch(hk_ctx* c, int layer_begin, int layer_end, int step, const voi
     a.n = c->tokens[step];
     a.H = c->H;
     a.row_bytes = row_bytes;
-    // Two tokens per workgroup (one when a token's rows exceed half a 16 KB
-    // block).  Measured on the 32-layer, 16-head, batch-4 full-cache appends:
-    // two tokens (8 KB per tensor) 5.43-5.47 TB/s against 5.29-5.33 with four
-    // (16 KB), 5.31 with three and 4.95-4.97 with one; at 28 heads, batch 16,
-    // two tokens (14 KB) 5.20 against 5.06-5.08 with one and 5.04 with three.
-    a.rows = std::max(1, std::min(hk::kRowsTokens, hk::kCopyBlockBytes / (c->H * row_bytes)));
+    // Tokens per workgroup: at least two and at least 8 KB per tensor, at
+    // most 16 KB (and at least one token).  Measured on the 32-layer,
+    // 16-head, batch-4 full-cache appends: two tokens (8 KB per tensor)
+    // 5.43-5.47 TB/s against 5.29-5.33 with four (16 KB), 5.31 with three and
+    // 4.95-4.97 with one; at 28 heads, batch 16, two tokens (14 KB) 5.20
+    // against 5.06-5.08 with one and 5.04 with three.
+    const int tok_bytes = c->H * row_bytes;
+    a.rows = std::max(1, std::min(hk::kCopyBlockBytes / tok_bytes,
+                                  std::max(hk::kRowsTokens, hk::kCopyBlockBytes / 2 / tok_bytes)));
     hipError_t e = hk::launch_compact_rows(a, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return hip_fail(e, "compact launch");
   } else if (last > first) {

@@ -20,7 +20,8 @@ namespace hk {
 // part is at most kGatherPartBytes of every row.  Scales that most heads
 // store are copied in token blocks (contiguous reads across all heads) when a
 // layer has at most kRowsMaxHeads heads (their destinations sit in LDS), at
-// most kRowsTokens tokens per workgroup.
+// least kRowsTokens tokens and half a block per workgroup where a block holds
+// that many.
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlockBytes = 16384;
 constexpr int kCopyBlockBytesLarge = 32768;
